@@ -1,0 +1,279 @@
+"""CPU oracle for the attention hot path: plain fp64 C behind a thin numpy/ctypes shim.
+
+TEST INFRASTRUCTURE ONLY -- the test-suite, the smoke check and the benchmark's CPU
+baseline are its only callers.  It shares no code with the GPU library.
+
+Every tensor crosses this shim as raw IEEE binary16 bits in ``numpy.uint16`` arrays
+(positions and lengths as ``int32``), with the layouts
+
+    q, out      [n, t, hq, d]        k, v (new)   [n, t, hkv, d]
+    positions   [n, t]               lens         [n]
+    cache_k/v   [n, hkv, s_cap, d]   (updated in place)
+
+The arithmetic lives in ``kvrope_oracle.c``; see its header for the passages of the pages
+each function follows.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import dataclasses
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+@dataclasses.dataclass(frozen=True)
+class RopeParams:
+    base: float = 10000.0
+    n_rot: int = 128
+    yarn: bool = False
+    freq_scale: float = 1.0
+    ext_factor: float = 0.0
+    n_ctx_orig: int = 4096
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    mscale: float = 1.0
+
+    @staticmethod
+    def plain(n_rot: int = 128, base: float = 10000.0) -> "RopeParams":
+        return RopeParams(base=base, n_rot=n_rot)
+
+    @staticmethod
+    def yarn_tail(n_rot: int = 64, base: float = 10000.0, factor: float = 4.0,
+                  n_ctx_orig: int = 4096, beta_fast: float = 32.0,
+                  beta_slow: float = 1.0) -> "RopeParams":
+        return RopeParams(base=base, n_rot=n_rot, yarn=True, freq_scale=1.0 / factor,
+                          ext_factor=1.0, n_ctx_orig=n_ctx_orig, beta_fast=beta_fast,
+                          beta_slow=beta_slow, mscale=1.0 + 0.1 * math.log(factor))
+
+
+class _CRope(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_double), ("n_rot", ctypes.c_int32), ("yarn", ctypes.c_int32),
+                ("freq_scale", ctypes.c_double), ("ext_factor", ctypes.c_double),
+                ("n_ctx_orig", ctypes.c_int32), ("beta_fast", ctypes.c_double),
+                ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double)]
+
+
+def _c_rope(rp: RopeParams) -> _CRope:
+    return _CRope(rp.base, rp.n_rot, int(rp.yarn), rp.freq_scale, rp.ext_factor,
+                  rp.n_ctx_orig, rp.beta_fast, rp.beta_slow, rp.mscale)
+
+
+_P = ctypes.c_void_p
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load an oracle library build and declare its C signatures."""
+    L = ctypes.CDLL(path)
+    L.ora_f16_to_f64.restype = ctypes.c_double
+    L.ora_f16_to_f64.argtypes = [ctypes.c_uint16]
+    L.ora_f64_to_f16.restype = ctypes.c_uint16
+    L.ora_f64_to_f16.argtypes = [ctypes.c_double]
+    L.ora_f16_to_f64_array.argtypes = [_P, _P, ctypes.c_int64]
+    L.ora_f64_to_f16_array.argtypes = [_P, _P, ctypes.c_int64]
+    L.ora_yarn_corr_dim.restype = ctypes.c_double
+    L.ora_yarn_corr_dim.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                    ctypes.c_double]
+    L.ora_yarn_ramp.restype = ctypes.c_double
+    L.ora_yarn_ramp.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_int]
+    L.ora_rope_freqs.argtypes = [ctypes.POINTER(_CRope), _P, _P, _P]
+    L.ora_rope.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                           ctypes.POINTER(_CRope), _P, _P]
+    L.ora_append.restype = ctypes.c_int
+    L.ora_append.argtypes = [_P, _P, _P, _P, _P] + [ctypes.c_int] * 5
+    L.ora_prefill_kv.restype = ctypes.c_int
+    L.ora_prefill_kv.argtypes = ([_P] * 8 + [ctypes.c_int] * 6 +
+                                 [ctypes.c_double, ctypes.POINTER(_CRope), _P, _P])
+    L.ora_decode.restype = ctypes.c_int
+    L.ora_decode.argtypes = ([_P] * 8 + [ctypes.c_int] * 5 +
+                             [ctypes.c_double, ctypes.POINTER(_CRope), _P, _P])
+    L.ora_decode_rows.argtypes = ([_P] * 6 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int64,
+                                              ctypes.c_double, _P])
+    L.ora_num_threads.restype = ctypes.c_int
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _lib = load(_build.LIB)
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Temporarily route every oracle call through another build (mutation tests)."""
+    global _lib
+    prev = lib()
+    _lib = load(path)
+    try:
+        yield
+    finally:
+        _lib = prev
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    assert a.dtype == np.uint16, a.dtype
+    return np.ascontiguousarray(a)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def num_threads() -> int:
+    return lib().ora_num_threads()
+
+
+# ---------------------------------------------------------------- f16 codec
+def f16_to_f64(h) -> np.ndarray:
+    h = _u16(h)
+    out = np.empty(h.shape, dtype=np.float64)
+    lib().ora_f16_to_f64_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def f64_to_f16(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().ora_f64_to_f16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+# ---------------------------------------------------------------- RoPE
+def yarn_corr_dim(n_dims: int, n_ctx_orig: int, beta: float, base: float) -> float:
+    return lib().ora_yarn_corr_dim(n_dims, n_ctx_orig, beta, base)
+
+
+def yarn_ramp(low: float, high: float, j: int) -> float:
+    return lib().ora_yarn_ramp(low, high, j)
+
+
+def rope_freqs(rp: RopeParams):
+    """Returns (omega_eff[n_rot/2], gamma[n_rot/2], (d0, d1))."""
+    half = rp.n_rot // 2
+    om = np.empty(max(half, 1), dtype=np.float64)
+    ga = np.empty(max(half, 1), dtype=np.float64)
+    dims = np.empty(2, dtype=np.float64)
+    c = _c_rope(rp)
+    lib().ora_rope_freqs(ctypes.byref(c), _ptr(om), _ptr(ga), _ptr(dims))
+    return om[:half], ga[:half], (float(dims[0]), float(dims[1]))
+
+
+def rope(x, positions, rp: RopeParams):
+    """x: [rows, h, d] f16 bits, positions: [rows].  Returns (rotated f16 bits, fp64)."""
+    x = _u16(x)
+    pos = _i32(positions)
+    rows, h, d = x.shape
+    assert pos.shape == (rows,)
+    out = np.empty_like(x)
+    out64 = np.empty(x.shape, dtype=np.float64)
+    c = _c_rope(rp)
+    lib().ora_rope(_ptr(x), _ptr(pos), rows, h, d, ctypes.byref(c), _ptr(out), _ptr(out64))
+    return out, out64
+
+
+# ---------------------------------------------------------------- cache append
+def append(cache_k: np.ndarray, cache_v: np.ndarray, k, v, lens) -> None:
+    """In place: rows [lens[n], lens[n]+t) of each cache get k / v (bit copy)."""
+    k, v, lens = _u16(k), _u16(v), _i32(lens)
+    n, t, hkv, d = k.shape
+    s_cap = cache_k.shape[2]
+    assert cache_k.shape == (n, hkv, s_cap, d) and cache_v.shape == cache_k.shape
+    rc = lib().ora_append(_ptr(cache_k), _ptr(cache_v), _ptr(k), _ptr(v), _ptr(lens),
+                          n, t, hkv, d, s_cap)
+    if rc != 0:
+        raise ValueError("oracle append: capacity exceeded")
+
+
+# ---------------------------------------------------------------- attention
+def prefill_kv(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens,
+               scale: float, rp: RopeParams):
+    """Chunked prefill over a history.  Caches are updated in place.
+
+    Returns (out f16 bits [n,t,hq,d], out fp64, rotated k fp64 [n,t,hkv,d])."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    pos, lens = _i32(positions), _i32(lens)
+    n, t, hq, d = q.shape
+    hkv = k.shape[2]
+    s_cap = cache_k.shape[2]
+    assert k.shape == (n, t, hkv, d) and v.shape == k.shape and pos.shape == (n, t)
+    assert cache_k.shape == (n, hkv, s_cap, d) and cache_v.shape == cache_k.shape
+    assert cache_k.dtype == np.uint16 and cache_k.flags["C_CONTIGUOUS"]
+    assert cache_v.dtype == np.uint16 and cache_v.flags["C_CONTIGUOUS"]
+    assert lens.shape == (n,)
+    out = np.empty(q.shape, dtype=np.uint16)
+    out64 = np.empty(q.shape, dtype=np.float64)
+    k64 = np.empty(k.shape, dtype=np.float64)
+    c = _c_rope(rp)
+    rc = lib().ora_prefill_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cache_k),
+                              _ptr(cache_v), _ptr(lens), _ptr(out), n, t, hq, hkv, d, s_cap,
+                              float(scale), ctypes.byref(c), _ptr(out64), _ptr(k64))
+    if rc != 0:
+        raise ValueError("oracle prefill_kv: shape or capacity error")
+    return out, out64, k64
+
+
+def prefill(q, k, v, positions, cache_k, cache_v, scale: float, rp: RopeParams):
+    n = np.asarray(q).shape[0]
+    return prefill_kv(q, k, v, positions, cache_k, cache_v, np.zeros(n, np.int32), scale, rp)
+
+
+def decode(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens, scale: float,
+           rp: RopeParams):
+    """One decode step.  q: [n, hq, d]; k, v: [n, hkv, d]; positions, lens: [n].
+
+    Caches are updated in place (row lens[n]).  Returns (out bits [n,hq,d], out fp64,
+    rotated k fp64 [n,hkv,d])."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    pos, lens = _i32(positions), _i32(lens)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    s_cap = cache_k.shape[2]
+    assert k.shape == (n, hkv, d) and v.shape == k.shape and pos.shape == (n,)
+    assert cache_k.shape == (n, hkv, s_cap, d) and cache_v.shape == cache_k.shape
+    assert cache_k.dtype == np.uint16 and cache_k.flags["C_CONTIGUOUS"]
+    out = np.empty(q.shape, dtype=np.uint16)
+    out64 = np.empty(q.shape, dtype=np.float64)
+    k64 = np.empty(k.shape, dtype=np.float64)
+    c = _c_rope(rp)
+    rc = lib().ora_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cache_k), _ptr(cache_v),
+                          _ptr(lens), _ptr(out), n, hq, hkv, d, s_cap, float(scale),
+                          ctypes.byref(c), _ptr(out64), _ptr(k64))
+    if rc != 0:
+        raise ValueError("oracle decode: shape or capacity error")
+    return out, out64, k64
+
+
+def decode_rows(q_rot, cache_k: np.ndarray, cache_v: np.ndarray, units, heads, lens_s,
+                hq: int, scale: float) -> np.ndarray:
+    """Sampled decode attention: for sample i, unit units[i], query head heads[i] with
+    rotated query q_rot[i] attends over rows 0..lens_s[i] of its KV head in caches that
+    already hold the appended row.  Returns fp64 [ns, d]."""
+    q_rot = _u16(q_rot)
+    us, hs, ls = _i32(units), _i32(heads), _i32(lens_s)
+    ns, d = q_rot.shape
+    n, hkv, s_cap, d2 = cache_k.shape
+    assert d2 == d and us.shape == (ns,) and hs.shape == (ns,) and ls.shape == (ns,)
+    assert np.all(ls + 1 <= s_cap) and np.all(us < n) and np.all(hs < hq)
+    out = np.empty((ns, d), dtype=np.float64)
+    lib().ora_decode_rows(_ptr(q_rot), _ptr(cache_k), _ptr(cache_v), _ptr(us), _ptr(hs),
+                          _ptr(ls), ns, hq, hkv, d, s_cap, float(scale), _ptr(out))
+    return out

@@ -1,0 +1,461 @@
+/*
+ * kvrope_oracle.c -- plain, slow, fp64 CPU reference for the attention hot path
+ * (rotary embedding of Q/K, KV-cache append, causal grouped-query attention in the
+ * prefill / prefill_kv / decode phases).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  It shares no code, header, table or
+ * helper with the GPU library; both sides only read the same seeded inputs.
+ *
+ * Sources (cited by page title and section):
+ *   [Sophgo]  "An MLIR-based LLM compilation method" (Sophgo TPU-MLIR paper):
+ *             sec. 2.2 (top.Rope, top.Concat, top.FAttention = scaled dot product + causal
+ *             mask), sec. 3.1 Listings 1-2 (block without / with history_k, history_v),
+ *             sec. 4.1 (the prefill / prefill_kv / decode split).
+ *   [ds4]     "ds4.c study notes", Part 4, section 1, Trace 1 (YaRN ramp and correction
+ *             dims) and Trace 2 (tail RoPE rotation, rotation matrix, theta schedule).
+ *   [Buddy]   "Buddy-MLIR DeepSeek model import, compilation and inference scheduling"
+ *             (juejin), sec. 6.4.3 (KV cache [B, kv_heads, max_len, head_dim], f16),
+ *             sec. 6.4.5-6.4.6 (cache hand-off: position = prompt length, +1 per step),
+ *             sec. 6.4.7 (an f16 decode done with a bf16 shift: why the codec here is
+ *             hand-written and checked against every bit pattern).
+ *   [CGDR]    "02 Prefill integration of CGDR" (MindSpore Qwen3.5 notes), sec. 1-2: the
+ *             unfused path expands KV heads with repeat_interleave, so query head h
+ *             reads KV head floor(h / G).
+ *
+ * Readings where the pages leave a step open are listed in the design doc; each one is also
+ * stated next to the code that takes it.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC (see build.py).
+ * Every floating-point step is fp64; f16 appears only at tensor boundaries.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------ */
+/* IEEE binary16 codec (fp64 <-> f16, round to nearest, ties to even).                   */
+/* Written arithmetically (frexp / ldexp / nearbyint), not by bit surgery.               */
+/* ------------------------------------------------------------------------------------ */
+
+double ora_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int m = h & 0x3ff;
+    double v;
+    if (e == 0x1f) {
+        v = (m == 0) ? INFINITY : NAN;
+    } else if (e == 0) {
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    } else {
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+uint16_t ora_f64_to_f16(double x)
+{
+    if (isnan(x))
+        return (uint16_t)(signbit(x) ? 0xfe00 : 0x7e00);
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    /* quantum of the f16 grid at the magnitude of a: 2^(max(E,-14)-10), E = floor(log2 a) */
+    int e2;
+    (void)frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1): E = e2 - 1 */
+    int E = e2 - 1;
+    if (E < -14)
+        E = -14;
+    const double quantum = ldexp(1.0, E - 10);
+    /* a / quantum is exact (power-of-two scaling); nearbyint rounds half to even */
+    const double n = nearbyint(a / quantum);
+    const double r = n * quantum; /* exact */
+    if (r >= 65536.0)              /* largest finite f16 is 65504; 65520 rounds up to inf */
+        return (uint16_t)(sign | 0x7c00);
+    /* encode r exactly */
+    if (r < ldexp(1.0, -14)) {
+        /* subnormal: r = k * 2^-24 */
+        const uint16_t k = (uint16_t)ldexp(r, 24);
+        return (uint16_t)(sign | k);
+    }
+    int re;
+    const double f = frexp(r, &re); /* r = f * 2^re, f in [0.5,1) */
+    const int biased = re - 1 + 15;
+    const uint16_t mant = (uint16_t)(ldexp(f, 11) - 1024.0); /* f*2^11 in [1024, 2048) */
+    return (uint16_t)(sign | (uint16_t)(biased << 10) | mant);
+}
+
+void ora_f16_to_f64_array(const uint16_t *h, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ora_f16_to_f64(h[i]);
+}
+
+void ora_f64_to_f16_array(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = ora_f64_to_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Rotary embedding parameters and per-pair frequencies.                                 */
+/* ------------------------------------------------------------------------------------ */
+
+typedef struct ora_rope_params {
+    double base;        /* theta base (10000 in every workload here) */
+    int32_t n_rot;      /* rotated dims per head (even); they are the LAST n_rot dims */
+    int32_t yarn;       /* 0: plain RoPE; 1: YaRN ramp between interpolated/extrapolated */
+    double freq_scale;  /* YaRN: 1 / scale factor */
+    double ext_factor;  /* YaRN: weight of the ramp */
+    int32_t n_ctx_orig; /* YaRN: original training context */
+    double beta_fast;   /* YaRN: correction-dim boundary (fast) */
+    double beta_slow;   /* YaRN: correction-dim boundary (slow) */
+    double mscale;      /* magnitude factor applied to both outputs of every rotated pair */
+} ora_rope_params;
+
+/* [ds4] Trace 1: the dimension index at which a pair turns `beta` full circles over the
+ * original context: n_dims * ln(n_ctx_orig / (2 pi beta)) / (2 ln base).
+ * Reading: n_dims is the rotated width n_rot; the value is used unrounded and unclamped
+ * (the page elides the body of the two-boundary helper). */
+double ora_yarn_corr_dim(int n_dims, int n_ctx_orig, double beta, double base)
+{
+    return (double)n_dims * log((double)n_ctx_orig / (2.0 * M_PI * beta)) / (2.0 * log(base));
+}
+
+/* [ds4] Trace 1: ramp over the pair index j = i0/2: 1 below `low` (keep the original
+ * frequency), 0 above `high` (fully scaled), linear in between.  The denominator is
+ * floored at 0.001 as on the page. */
+double ora_yarn_ramp(double low, double high, int j)
+{
+    double y = ((double)j - low) / fmax(0.001, high - low);
+    if (y < 0.0)
+        y = 0.0;
+    if (y > 1.0)
+        y = 1.0;
+    return 1.0 - y;
+}
+
+/* Per-pair effective angular frequency omega_eff[j], j = 0 .. n_rot/2 - 1.
+ * [ds4] Trace 2: theta = pos * base^(-2 j / n_rot) for pair j (the exponent uses the
+ * rotated width n_rot, so the tail rotation has its own schedule).
+ * YaRN reading (the page gives this step only as a comment): the ramp value
+ * gamma = ext_factor * ramp(d0, d1, j) mixes the interpolated frequency freq_scale*omega
+ * with the original omega: omega_eff = omega * (freq_scale * (1 - gamma) + gamma).
+ * Reading: the angle is pos * omega_eff (the position multiplies the effective frequency).
+ * gamma_out (optional) receives gamma; dims_out (optional) receives d0, d1. */
+void ora_rope_freqs(const ora_rope_params *rp, double *omega_eff, double *gamma_out,
+                    double *dims_out)
+{
+    const int half = rp->n_rot / 2;
+    double d0 = 0.0, d1 = 0.0;
+    if (rp->yarn) {
+        d0 = ora_yarn_corr_dim(rp->n_rot, rp->n_ctx_orig, rp->beta_fast, rp->base);
+        d1 = ora_yarn_corr_dim(rp->n_rot, rp->n_ctx_orig, rp->beta_slow, rp->base);
+    }
+    if (dims_out) {
+        dims_out[0] = d0;
+        dims_out[1] = d1;
+    }
+    for (int j = 0; j < half; ++j) {
+        const double omega = pow(rp->base, -2.0 * (double)j / (double)rp->n_rot);
+        double gamma = 1.0;
+        double w = omega;
+        if (rp->yarn) {
+            gamma = rp->ext_factor * ora_yarn_ramp(d0, d1, j);
+            w = omega * (rp->freq_scale * (1.0 - gamma) + gamma);
+        }
+        omega_eff[j] = w;
+        if (gamma_out)
+            gamma_out[j] = gamma;
+    }
+}
+
+/* Rotate rows of x in place of a copy.
+ * x, out: f16 [rows, h, d] (row-major, d innermost); positions: [rows].
+ * [ds4] Trace 2 rotation of pair (x0, x1) = (x[o + 2j], x[o + 2j + 1]) with o = d - n_rot:
+ *     c = cos(theta) * mscale,  s = sin(theta) * mscale,
+ *     x0' = x0 * c - x1 * s,    x1' = x0 * s + x1 * c
+ * i.e. the matrix [[cos, -sin], [sin, cos]] applied to adjacent pairs.
+ * Reading: the rotated dims are the last n_rot dims of each head (the page's pointer to
+ * the head start contradicts its own "tail" wording and the tail-rotation workload).
+ * Dims [0, o) are copied bit for bit.  out64 (optional) gets the unrounded fp64 values. */
+void ora_rope(const uint16_t *x, const int32_t *positions, int64_t rows, int h, int d,
+              const ora_rope_params *rp, uint16_t *out, double *out64)
+{
+    const int half = rp->n_rot / 2;
+    const int o = d - rp->n_rot;
+    double *omega = (double *)malloc(sizeof(double) * (size_t)(half > 0 ? half : 1));
+    ora_rope_freqs(rp, omega, NULL, NULL);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double pos = (double)positions[r];
+        for (int hh = 0; hh < h; ++hh) {
+            const int64_t base_idx = (r * h + hh) * (int64_t)d;
+            for (int i = 0; i < o; ++i) {
+                out[base_idx + i] = x[base_idx + i];
+                if (out64)
+                    out64[base_idx + i] = ora_f16_to_f64(x[base_idx + i]);
+            }
+            for (int j = 0; j < half; ++j) {
+                const double theta = pos * omega[j];
+                const double c = cos(theta) * rp->mscale;
+                const double s = sin(theta) * rp->mscale;
+                const int64_t i0 = base_idx + o + 2 * j;
+                const double x0 = ora_f16_to_f64(x[i0]);
+                const double x1 = ora_f16_to_f64(x[i0 + 1]);
+                const double y0 = x0 * c - x1 * s;
+                const double y1 = x0 * s + x1 * c;
+                out[i0] = ora_f64_to_f16(y0);
+                out[i0 + 1] = ora_f64_to_f16(y1);
+                if (out64) {
+                    out64[i0] = y0;
+                    out64[i0 + 1] = y1;
+                }
+            }
+        }
+    }
+    free(omega);
+}
+
+/* [Buddy] sec. 6.4.5 / [Sophgo] Listing 2 (Concat(history, new)):
+ * cache_k[n, g, lens[n] + t, :] = k[n, t, g, :], same for v; every other row unchanged.
+ * Caches: [n, hkv, s_cap, d]; k, v: [n, t, hkv, d].  Returns -1 (and writes nothing) if
+ * any lens[n] + t exceeds s_cap: no silent clamping. */
+int ora_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k, const uint16_t *v,
+               const int32_t *lens, int n, int t, int hkv, int d, int s_cap)
+{
+    for (int u = 0; u < n; ++u)
+        if (lens[u] < 0 || (int64_t)lens[u] + t > s_cap)
+            return -1;
+    for (int u = 0; u < n; ++u)
+        for (int tt = 0; tt < t; ++tt)
+            for (int g = 0; g < hkv; ++g) {
+                const int64_t dst = (((int64_t)u * hkv + g) * s_cap + lens[u] + tt) * d;
+                const int64_t src = (((int64_t)u * t + tt) * hkv + g) * d;
+                memcpy(cache_k + dst, k + src, sizeof(uint16_t) * (size_t)d);
+                memcpy(cache_v + dst, v + src, sizeof(uint16_t) * (size_t)d);
+            }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Attention.                                                                            */
+/* ------------------------------------------------------------------------------------ */
+
+/* prefill_kv ([Sophgo] Listing 2 and sec. 4.1; prefill is the case lens == 0, Listing 1):
+ *   1. rotate q and k at their positions; the rotated q and k are rounded to f16 because
+ *      the Rope op hands f16 tensors to the attention op in an f16 model;
+ *   2. append rotated k and raw v at rows [lens[n], lens[n] + t) of the cache;
+ *   3. for query token tt of unit n and query head hq, with g = hq / (h_q / h_kv)
+ *      ([CGDR] repeat_interleave head mapping), attend over cache rows j = 0 .. lens[n]+tt
+ *      (the causal mask over the concatenation [history; new]):
+ *         s_j = scale * <q_hat, K_j>,  p = softmax(s),  o = sum_j p_j V_j.
+ * This implementation builds the full masked score matrix of each (unit, head) and then
+ * normalises each row; the decode function below is written as a per-query loop instead.
+ * q, out: [n, t, hq, d]; k, v: [n, t, hkv, d]; positions: [n, t]; lens: [n] (host);
+ * caches: [n, hkv, s_cap, d] (updated in place).  out64 (optional): unrounded output.
+ * k64 (optional): unrounded rotated k, [n, t, hkv, d].  Returns 0, or -1 on a capacity
+ * or shape error (nothing written). */
+int ora_prefill_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const int32_t *positions, uint16_t *cache_k, uint16_t *cache_v,
+                   const int32_t *lens, uint16_t *out, int n, int t, int hq, int hkv, int d,
+                   int s_cap, double scale, const ora_rope_params *rp, double *out64,
+                   double *k64)
+{
+    if (hkv <= 0 || hq % hkv != 0)
+        return -1;
+    for (int u = 0; u < n; ++u)
+        if (lens[u] < 0 || (int64_t)lens[u] + t > s_cap)
+            return -1;
+    const int G = hq / hkv;
+    const int64_t qn = (int64_t)n * t * hq * d, kn = (int64_t)n * t * hkv * d;
+    uint16_t *qh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(qn > 0 ? qn : 1));
+    uint16_t *kh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(kn > 0 ? kn : 1));
+    ora_rope(q, positions, (int64_t)n * t, hq, d, rp, qh, NULL);
+    ora_rope(k, positions, (int64_t)n * t, hkv, d, rp, kh, k64);
+    ora_append(cache_k, cache_v, kh, v, lens, n, t, hkv, d, s_cap);
+
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int u = 0; u < n; ++u) {
+        for (int h = 0; h < hq; ++h) {
+            const int g = h / G;
+            const int L = lens[u] + t; /* keys visible to the last query */
+            const uint16_t *Kc = cache_k + ((int64_t)u * hkv + g) * s_cap * d;
+            const uint16_t *Vc = cache_v + ((int64_t)u * hkv + g) * s_cap * d;
+            double *S = (double *)malloc(sizeof(double) * (size_t)t * (size_t)(L > 0 ? L : 1));
+            double *qd = (double *)malloc(sizeof(double) * (size_t)d);
+            /* masked score matrix */
+            for (int tt = 0; tt < t; ++tt) {
+                const uint16_t *qrow = qh + (((int64_t)u * t + tt) * hq + h) * d;
+                for (int i = 0; i < d; ++i)
+                    qd[i] = ora_f16_to_f64(qrow[i]);
+                for (int j = 0; j < L; ++j) {
+                    if (j > lens[u] + tt) {
+                        S[(int64_t)tt * L + j] = -INFINITY;
+                        continue;
+                    }
+                    double acc = 0.0;
+                    for (int i = 0; i < d; ++i)
+                        acc += qd[i] * ora_f16_to_f64(Kc[(int64_t)j * d + i]);
+                    S[(int64_t)tt * L + j] = scale * acc;
+                }
+            }
+            /* row softmax and P V */
+            for (int tt = 0; tt < t; ++tt) {
+                double *row = S + (int64_t)tt * L;
+                double mx = -INFINITY;
+                for (int j = 0; j < L; ++j)
+                    if (row[j] > mx)
+                        mx = row[j];
+                double sum = 0.0;
+                for (int j = 0; j < L; ++j) {
+                    row[j] = (row[j] == -INFINITY) ? 0.0 : exp(row[j] - mx);
+                    sum += row[j];
+                }
+                for (int j = 0; j < L; ++j)
+                    row[j] /= sum;
+                uint16_t *orow = out + (((int64_t)u * t + tt) * hq + h) * d;
+                for (int i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < L; ++j)
+                        acc += row[j] * ora_f16_to_f64(Vc[(int64_t)j * d + i]);
+                    orow[i] = ora_f64_to_f16(acc);
+                    if (out64)
+                        out64[(((int64_t)u * t + tt) * hq + h) * d + i] = acc;
+                }
+            }
+            free(qd);
+            free(S);
+        }
+    }
+    free(qh);
+    free(kh);
+    return 0;
+}
+
+/* decode ([Sophgo] sec. 4.1: one query per sequence, attending over every earlier key;
+ * [Buddy] sec. 6.4.5-6.4.6: the new token sits at the current cache length, which then
+ * grows by one).  For unit n: rotate q[n] and k[n] at positions[n], write the rotated k
+ * and v at cache row lens[n], then for each query head attend over rows 0 .. lens[n].
+ * Written as a per-query loop over the cache (max, then exp-sum, then weighted sum).
+ * q, out: [n, hq, d]; k, v: [n, hkv, d]; positions, lens: [n] (host).
+ * Returns 0, or -1 (nothing written) on a capacity / shape error. */
+int ora_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+               const int32_t *positions, uint16_t *cache_k, uint16_t *cache_v,
+               const int32_t *lens, uint16_t *out, int n, int hq, int hkv, int d, int s_cap,
+               double scale, const ora_rope_params *rp, double *out64, double *k64)
+{
+    if (hkv <= 0 || hq % hkv != 0)
+        return -1;
+    for (int u = 0; u < n; ++u)
+        if (lens[u] < 0 || (int64_t)lens[u] + 1 > s_cap)
+            return -1;
+    const int G = hq / hkv;
+    uint16_t *qh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)((int64_t)n * hq * d + 1));
+    uint16_t *kh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)((int64_t)n * hkv * d + 1));
+    ora_rope(q, positions, n, hq, d, rp, qh, NULL);
+    ora_rope(k, positions, n, hkv, d, rp, kh, k64);
+    ora_append(cache_k, cache_v, kh, v, lens, n, 1, hkv, d, s_cap);
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int u = 0; u < n; ++u) {
+        for (int h = 0; h < hq; ++h) {
+            const int g = h / G;
+            const int nk = lens[u] + 1;
+            const uint16_t *Kc = cache_k + ((int64_t)u * hkv + g) * s_cap * d;
+            const uint16_t *Vc = cache_v + ((int64_t)u * hkv + g) * s_cap * d;
+            const uint16_t *qrow = qh + ((int64_t)u * hq + h) * d;
+            double *qd = (double *)malloc(sizeof(double) * (size_t)d);
+            double *s = (double *)malloc(sizeof(double) * (size_t)nk);
+            double *acc = (double *)calloc((size_t)d, sizeof(double));
+            for (int i = 0; i < d; ++i)
+                qd[i] = ora_f16_to_f64(qrow[i]);
+            double mx = -INFINITY;
+            for (int j = 0; j < nk; ++j) {
+                double dot = 0.0;
+                for (int i = 0; i < d; ++i)
+                    dot += qd[i] * ora_f16_to_f64(Kc[(int64_t)j * d + i]);
+                s[j] = scale * dot;
+                if (s[j] > mx)
+                    mx = s[j];
+            }
+            double denom = 0.0;
+            for (int j = 0; j < nk; ++j) {
+                const double e = exp(s[j] - mx);
+                denom += e;
+                for (int i = 0; i < d; ++i)
+                    acc[i] += e * ora_f16_to_f64(Vc[(int64_t)j * d + i]);
+            }
+            uint16_t *orow = out + ((int64_t)u * hq + h) * d;
+            for (int i = 0; i < d; ++i) {
+                const double val = acc[i] / denom;
+                orow[i] = ora_f64_to_f16(val);
+                if (out64)
+                    out64[((int64_t)u * hq + h) * d + i] = val;
+            }
+            free(acc);
+            free(s);
+            free(qd);
+        }
+    }
+    free(qh);
+    free(kh);
+    return 0;
+}
+
+/* Decode attention for a subset of (unit, head) rows only, reading a cache that already
+ * holds the appended row (used to check very large workloads by sampling).  For each
+ * sample i: unit us[i], head hs[i]; q_rot: that row's rotated f16 query [d].
+ * Attends over cache rows 0 .. lens_s[i] (inclusive) of KV head hs[i] / G. */
+void ora_decode_rows(const uint16_t *q_rot, const uint16_t *cache_k, const uint16_t *cache_v,
+                     const int32_t *us, const int32_t *hs, const int32_t *lens_s, int64_t ns,
+                     int hq, int hkv, int d, int64_t s_cap, double scale, double *out64)
+{
+    const int G = hq / hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < ns; ++i) {
+        const int g = hs[i] / G;
+        const int nk = lens_s[i] + 1;
+        const uint16_t *Kc = cache_k + ((int64_t)us[i] * hkv + g) * s_cap * d;
+        const uint16_t *Vc = cache_v + ((int64_t)us[i] * hkv + g) * s_cap * d;
+        const uint16_t *qrow = q_rot + i * d;
+        double *acc = (double *)calloc((size_t)d, sizeof(double));
+        double *s = (double *)malloc(sizeof(double) * (size_t)nk);
+        double mx = -INFINITY;
+        for (int j = 0; j < nk; ++j) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += ora_f16_to_f64(qrow[e]) * ora_f16_to_f64(Kc[(int64_t)j * d + e]);
+            s[j] = scale * dot;
+            if (s[j] > mx)
+                mx = s[j];
+        }
+        double denom = 0.0;
+        for (int j = 0; j < nk; ++j) {
+            const double w = exp(s[j] - mx);
+            denom += w;
+            for (int e = 0; e < d; ++e)
+                acc[e] += w * ora_f16_to_f64(Vc[(int64_t)j * d + e]);
+        }
+        for (int e = 0; e < d; ++e)
+            out64[i * d + e] = acc[e] / denom;
+        free(s);
+        free(acc);
+    }
+}
+
+int ora_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,99 @@
+"""The oracle's pins must be strong enough to catch plausible mistakes.
+
+Each case plants one mistake in a private copy of the oracle's C source (on the CPU),
+builds it, routes the oracle through that build and runs the pins that should object.
+A mutant that passes every listed pin fails this test.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+
+from tests import test_oracle_attention as A
+from tests import test_oracle_codec as C
+from tests import test_oracle_rope as R
+
+MUTANTS = [
+    ("rotation sign", "const double y0 = x0 * c - x1 * s;", "const double y0 = x0 * c + x1 * s;",
+     [R.test_pair_norm_scaled_by_mscale_only, R.test_pair0_turns_by_position_radians_textbook]),
+    ("rotation direction",
+     "const double y0 = x0 * c - x1 * s;\n                const double y1 = x0 * s + x1 * c;",
+     "const double y0 = x0 * c + x1 * s;\n                const double y1 = -x0 * s + x1 * c;",
+     [R.test_pair0_turns_by_position_radians_textbook, R.test_plain_matches_complex_multiplication]),
+    ("frequency exponent", "-2.0 * (double)j / (double)rp->n_rot", "-1.0 * (double)j / (double)rp->n_rot",
+     [R.test_frequency_schedule_textbook, R.test_plain_matches_complex_multiplication]),
+    ("exponent uses head dim", "-2.0 * (double)j / (double)rp->n_rot", "-2.0 * (double)j / 128.0",
+     [R.test_tail_half_width_schedule]),
+    ("rotate the head start", "const int o = d - rp->n_rot;", "const int o = 0;",
+     [R.test_tail_half_width_schedule, R.test_yarn_position_zero_scales_by_mscale]),
+    ("YaRN mix swapped", "w = omega * (rp->freq_scale * (1.0 - gamma) + gamma);",
+     "w = omega * (rp->freq_scale * gamma + (1.0 - gamma));",
+     [R.test_yarn_limits_equal_plain_rotation]),
+    ("mscale dropped", "const double c = cos(theta) * rp->mscale;", "const double c = cos(theta);",
+     [R.test_pair_norm_scaled_by_mscale_only, R.test_yarn_position_zero_scales_by_mscale]),
+    ("corr dim without 2", "(2.0 * M_PI * beta)", "(M_PI * beta)",
+     [R.test_yarn_correction_dims_turn_beta_circles]),
+    ("ramp inverted", "    return 1.0 - y;", "    return y;",
+     [R.test_yarn_ramp_endpoints_and_linearity]),
+    ("causal mask off by one", "if (j > lens[u] + tt) {", "if (j >= lens[u] + tt && j > 0) {",
+     [A.test_zero_query_gives_prefix_mean, A.test_brute_force_torch_float64]),
+    ("no causal mask", "if (j > lens[u] + tt) {", "if (0) {",
+     [A.test_zero_query_gives_prefix_mean]),
+    ("GQA head mapping", "const int g = h / G;", "const int g = h % hkv;",
+     [A.test_brute_force_torch_float64, A.test_single_token_returns_its_value_row]),
+    ("scale dropped", "S[(int64_t)tt * L + j] = scale * acc;", "S[(int64_t)tt * L + j] = acc;",
+     [A.test_brute_force_torch_float64]),
+    ("softmax not normalised", "row[j] /= sum;", "row[j] /= 1.0;",
+     [A.test_probabilities_sum_to_one]),
+    ("decode skips the new key", "const int nk = lens[u] + 1;", "const int nk = lens[u] > 0 ? lens[u] : 1;",
+     [A.test_prefill_equals_successive_decodes]),
+    ("append at row 0", "const int64_t dst = (((int64_t)u * hkv + g) * s_cap + lens[u] + tt) * d;",
+     "const int64_t dst = (((int64_t)u * hkv + g) * s_cap + tt) * d;",
+     [A.test_append_writes_only_its_rows]),
+    ("rounding truncates", "nearbyint(a / quantum)", "floor(a / quantum)",
+     [C.test_encode_midpoints_ties_to_even]),
+    ("f16 decode as bf16-style shift", "v = ldexp((double)(m + 1024), e - 25);",
+     "v = ldexp((double)(m + 1024), e - 24);",
+     [C.test_decode_every_bit_pattern]),
+]
+
+
+def _param_args(fn):
+    """Default arguments for the parametrised pins (first parameter set)."""
+    marks = getattr(fn, "pytestmark", [])
+    for m in marks:
+        if m.name == "parametrize":
+            names = [x.strip() for x in m.args[0].split(",")] if isinstance(m.args[0], str) \
+                else list(m.args[0])
+            vals = m.args[1][0]
+            if len(names) == 1:
+                vals = (vals,)
+            return dict(zip(names, vals))
+    return {}
+
+
+def _detects(fn) -> bool:
+    try:
+        fn(oracle, **_param_args(fn))
+    except (AssertionError, ValueError, FloatingPointError):
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name,old,new,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, pins):
+    src = open(obuild.SRC).read()
+    assert src.count(old) >= 1, "mutation site not found: " + name
+    mutated = src.replace(old, new)
+    with tempfile.TemporaryDirectory() as td:
+        cpath = os.path.join(td, "m.c")
+        lpath = os.path.join(td, "libm.so")
+        open(cpath, "w").write(mutated)
+        subprocess.run(["gcc", *obuild.CFLAGS, cpath, "-o", lpath, "-lm"], check=True)
+        with oracle.use_library(lpath):
+            caught = [p.__name__ for p in pins if _detects(p)]
+    assert caught, "no pin caught the planted mistake: " + name
