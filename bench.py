@@ -1,0 +1,237 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+
+One step is one attn_prefill call (rotary embedding of k + cache append, then causal GQA
+flash attention with q rotated in the kernel prologue) over the 28-layer, T = 1024,
+12q/2kv x 128 prefill workload, with every input already resident in HBM.  `value` is
+the prefill attention throughput in TFLOP/s, counting 4 * head_dim FLOPs per unmasked
+(query, key) pair per query head (the two GEMMs; softmax and rotation not counted).
+
+The same run also measures the decode side of the metric -- KV-cache GB/s of one
+attn_decode step on the 28-layer batch-32 (4096-row) workload and on the 4-layer
+batch-64 YaRN long-context workload -- with the 256 MB Infinity Cache flushed before
+every timed step; decode bytes count the cache rows read plus the new k/v read, the
+appended row written and q read / out written.
+
+`roofline` describes the dominant kernel (the prefill flash kernel), timed per launch
+with HIP events the library records around it on the launch stream; `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same prefill workload.
+Rank 0 prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (% MFMA peak) + decode KV-cache GB/s (% HBM peak)"
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense f16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(n, t, hq, d, hist):
+    """4*d FLOPs per unmasked (query, key) pair per query head."""
+    pairs = 0
+    for h0 in hist:
+        pairs += t * (t + 1) // 2 + int(h0) * t
+    return 4.0 * d * hq * pairs
+
+
+def decode_bytes(lens, hq, hkv, d):
+    lens = [int(x) for x in lens]
+    per_unit_fixed = 2 * hkv * d * 2 + 2 * hkv * d * 2 + 2 * hq * d * 2
+    return sum(2 * hkv * d * 2 * L for L in lens) + per_unit_fixed * len(lens)
+
+
+def make_events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()   # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    return evs
+
+
+def bench_prefill(kv, W, name, steps, warmup):
+    import torch
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg, device="cuda")
+    rp = kv.RopeParams.from_fields(cfg.rope)
+    out = torch.empty_like(inp.q)
+    hist = inp.lens.cpu().numpy()
+    call = (lambda: kv.prefill(inp.q, inp.k, inp.v, inp.positions, inp.cache_k, inp.cache_v, rp,
+                               scale=cfg.scale, out=out)) if cfg.phase == "prefill" else \
+        (lambda: kv.prefill_kv(inp.q, inp.k, inp.v, inp.positions, inp.cache_k, inp.cache_v,
+                               inp.lens, int(hist.max()), rp, scale=cfg.scale, out=out))
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # whole-step throughput: K back-to-back steps
+    t0, t1 = make_events(2)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # per-launch duration of the flash kernel (events recorded by the library)
+    evb, eva = make_events(steps), make_events(steps)
+    for i in range(steps):
+        kv.set_profile_events(evb[i], eva[i])
+        call()
+    torch.cuda.synchronize()
+    k_ms = sum(evb[i].elapsed_time(eva[i]) for i in range(steps)) / steps
+    flops = prefill_flops(cfg.n, cfg.t, cfg.hq, cfg.d, hist)
+    return cfg, ms_step, k_ms, flops
+
+
+def bench_decode(kv, W, name, steps, warmup):
+    import torch
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg, device="cuda")
+    rp = kv.RopeParams.from_fields(cfg.rope)
+    lens = inp.lens.cpu().numpy()
+    max_len = int(lens.max())
+    ws = torch.empty(max(kv.workspace_size(cfg.n, cfg.hq, cfg.hkv, max_len), 16), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(inp.q)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def call():
+        kv.decode(inp.q, inp.k, inp.v, inp.positions, inp.cache_k, inp.cache_v, inp.lens, max_len,
+                  rp, scale=cfg.scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ca, cb = make_events(steps), make_events(steps)
+    evb, eva = make_events(steps), make_events(steps)
+    for i in range(steps):
+        flush.fill_(i & 0xff)          # evict the Infinity Cache between steps
+        ca[i].record()
+        kv.set_profile_events(evb[i], eva[i])
+        call()
+        cb[i].record()
+    torch.cuda.synchronize()
+    call_ms = sum(ca[i].elapsed_time(cb[i]) for i in range(steps)) / steps
+    k_ms = sum(evb[i].elapsed_time(eva[i]) for i in range(steps)) / steps
+    nbytes = decode_bytes(lens, cfg.hq, cfg.hkv, cfg.d)
+    del inp, flush, ws
+    torch.cuda.empty_cache()
+    return cfg, call_ms, k_ms, nbytes
+
+
+def cpu_baseline(W, name, units):
+    """The oracle (untuned, fp64, OpenMP) on `units` layers of the prefill workload."""
+    import numpy as np
+    import oracle
+    cfg = W.CONFIGS[name]
+    inp = W.make_inputs(cfg, n=units)
+    bits = lambda x: x.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    ck, cv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    r = cfg.rope
+    rp = oracle.RopeParams(base=r.base, n_rot=r.n_rot, yarn=r.yarn, freq_scale=r.freq_scale,
+                           ext_factor=r.ext_factor, n_ctx_orig=r.n_ctx_orig, beta_fast=r.beta_fast,
+                           beta_slow=r.beta_slow, mscale=r.mscale)
+    t0 = time.perf_counter()
+    oracle.prefill_kv(bits(inp.q), bits(inp.k), bits(inp.v), inp.positions.numpy(), ck, cv,
+                      inp.lens.numpy(), cfg.scale, rp)
+    sec = time.perf_counter() - t0
+    flops = prefill_flops(units, cfg.t, cfg.hq, cfg.d, inp.lens.numpy())
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{units} of {cfg.n} layers of {name} (T={cfg.t}, {cfg.hq}q/{cfg.hkv}kv x "
+                      f"{cfg.d}), full causal prefill incl. rotary + append, {sec:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen1p5b_prefill_t1024")
+    ap.add_argument("--cpu-units", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention path runs on a single MI355X "
+              "(no collectives); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_causal_rope_amd as kv
+    from kv_cache_causal_rope_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    kv.lib()
+
+    log(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    cfg, ms_step, k_ms, flops = bench_prefill(kv, W, args.workload, args.steps, args.warmup)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    log(f"[bench] prefill: {ms_step * 1e3:.1f} us/step, flash kernel {k_ms * 1e3:.1f} us, "
+        f"{value:.1f} TFLOP/s step, {achieved:.1f} TFLOP/s kernel")
+    torch.cuda.empty_cache()
+
+    decode = []
+    if not args.no_decode:
+        for name in ["qwen1p5b_decode_l4096_b32", "yarn_decode_l32k_b64"]:
+            log(f"[bench] decode {name}")
+            dcfg, call_ms, dk_ms, nbytes = bench_decode(kv, W, name, max(3, args.steps // 2),
+                                                        min(args.warmup, 3))
+            gbs = nbytes / (call_ms * 1e-3) / 1e9
+            kgbs = nbytes / (dk_ms * 1e-3) / 1e9
+            log(f"[bench] decode {name}: {call_ms * 1e3:.1f} us/step, split kernel "
+                f"{dk_ms * 1e3:.1f} us, {gbs:.0f} GB/s step, {kgbs:.0f} GB/s kernel")
+            decode.append({"workload": name, "value": round(gbs, 1), "unit": "GB/s",
+                           "ms_per_step": round(call_ms, 4), "bytes_per_step": nbytes,
+                           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                           "roofline": {"bound": "hbm", "achieved": round(kgbs, 1),
+                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None}})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_units} layers")
+        cpu = cpu_baseline(W, args.workload, args.cpu_units)
+        log(f"[bench] cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch, "t": cfg.t,
+                   "hq": cfg.hq, "hkv": cfg.hkv, "head_dim": cfg.d, "rope": "plain base 1e4",
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": None},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * kvrope.h -- C ABI of the MI355X (gfx950) attention hot path: rotary embedding of
+ * Q/K (plain RoPE or the YaRN-ramped tail rotation), KV-cache append, and causal
+ * grouped-query attention in the three phases prefill, prefill_kv and decode.
+ *
+ * Sources (cited by page and section):
+ *   [Sophgo] "An MLIR-based LLM compilation method" (Sophgo TPU-MLIR paper): sec. 2.2
+ *            (top.Rope, top.Concat, top.FAttention = scaled dot product + causal mask),
+ *            sec. 3.1 Listing 1 (block without history), Listing 2 (block with
+ *            history_k / history_v and Concat(history, new)), sec. 4 and 4.1 (the
+ *            prefill / prefill_kv / decode split).
+ *   [ds4]    "ds4.c study notes", Part 4 sec. 1: Trace 1 (YaRN ramp, correction dims),
+ *            Trace 2 (tail rotation of the last n_rot dims, theta schedule, matrix).
+ *   [Buddy]  "Buddy-MLIR DeepSeek model import, compilation and inference scheduling"
+ *            (juejin): sec. 6.4.3 (per-layer cache [B, kv_heads, max_len, head_dim] f16),
+ *            sec. 6.4.5 (prompt rows copied into the decode cache, position = prompt
+ *            length), sec. 6.4.6 (decode position grows by one per step), sec. 5.4.2
+ *            and 9.2 (results returned through caller-provided memory).
+ *   [CGDR]   "02 Prefill integration of CGDR" (MindSpore Qwen3.5 notes): sec. 1-2
+ *            (KV heads shared by query-head groups via repeat_interleave; flat
+ *            [tokens, heads, head_dim] f16 at the kernel boundary), sec. 6 (a
+ *            hard-coded softmax scale as a silent-error hazard: here it is an argument).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers.  f16 tensors are IEEE binary16 bit patterns
+ *     (uint16_t storage), dense, row-major, innermost dimension last:
+ *         q, out            [n, t, hq, d]
+ *         k, v (new rows)   [n, t, hkv, d]
+ *         cache_k, cache_v  [n, hkv, s_cap, d]
+ *         positions         [n, t]   int32
+ *         lens              [n]      int32   (valid history rows per unit)
+ *     n counts independent units (layers x sequences); every unit has its own cache.
+ *   - Query head h reads KV head h / (hq / hkv).  hq must be a multiple of hkv.
+ *   - d must be 128.  Tensor pointers must be 16-byte aligned.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     never synchronises.  The caller owns every buffer; the library allocates and frees
+ *     no device memory and keeps no per-call state.
+ *   - Return value: KVROPE_OK (0) or a negative status.  Every status except
+ *     KVROPE_ERR_HIP is decided on the host before any HIP call, so on error nothing has
+ *     been launched and no buffer has been touched.  No call clamps silently.
+ *   - Lengths and positions live in device memory and are not read by the host.  The
+ *     host checks the capacity with the caller's bound `max_len` (>= every lens[u]).  A
+ *     kernel that finds lens[u] < 0 or lens[u] > max_len writes no cache row of unit u
+ *     and fills that unit's output with NaN, so a wrong bound never writes out of bounds.
+ *   - `out` must not overlap q, k, v or the caches.
+ */
+#ifndef KVROPE_H
+#define KVROPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVROPE_OK 0
+#define KVROPE_ERR_NULL (-1)      /* a required pointer is NULL */
+#define KVROPE_ERR_SHAPE (-2)     /* negative size, d != 128, hq % hkv != 0, hkv < 1 */
+#define KVROPE_ERR_ROPE (-3)      /* n_rot odd / < 2 / > d, base <= 1, bad YaRN field */
+#define KVROPE_ERR_CAPACITY (-4)  /* max_len + t > s_cap, or max_len < 0 */
+#define KVROPE_ERR_ALIGN (-5)     /* a tensor pointer is not 16-byte aligned */
+#define KVROPE_ERR_WORKSPACE (-6) /* workspace smaller than kvrope_workspace_size() */
+#define KVROPE_ERR_SCALE (-7)     /* softmax scale not finite or <= 0 */
+#define KVROPE_ERR_HIP (-8)       /* a HIP launch failed (see kvrope_last_hip_error) */
+
+/* Rotary embedding parameters ([ds4] Traces 1-2).
+ * Pair j = 0 .. n_rot/2-1 of a head rotates dims (d - n_rot + 2j, d - n_rot + 2j + 1)
+ * by theta = pos * w_j with
+ *     w_j = base^(-2j / n_rot)                                   (plain)
+ *     w_j = base^(-2j / n_rot) * (freq_scale * (1 - g_j) + g_j)   (yarn)
+ *     g_j = ext_factor * ramp(c(beta_fast), c(beta_slow), j)
+ *     c(beta) = n_rot * ln(n_ctx_orig / (2 pi beta)) / (2 ln base)
+ *     ramp(lo, hi, j) = 1 - clamp((j - lo) / max(0.001, hi - lo), 0, 1)
+ * and the pair (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c) with c = cos(theta) * mscale,
+ * s = sin(theta) * mscale.  Dims [0, d - n_rot) are left unchanged.  Plain RoPE over a
+ * whole head is n_rot = d, yarn = 0, mscale = 1. */
+typedef struct kvrope_rope_params {
+    double base;        /* > 1 (10000 in the workloads) */
+    int32_t n_rot;      /* even, 2 .. d */
+    int32_t yarn;       /* 0 = plain, 1 = YaRN ramp */
+    double freq_scale;  /* yarn: 1 / scale factor, > 0 */
+    double ext_factor;  /* yarn: ramp weight, in [0, 1] */
+    int32_t n_ctx_orig; /* yarn: > 0 */
+    double beta_fast;   /* yarn: > 0 */
+    double beta_slow;   /* yarn: > 0 */
+    double mscale;      /* finite, > 0 */
+} kvrope_rope_params;
+
+/* attn_rope_apply -- rotate x in place ([Sophgo] Listings 1-2: top.Rope(x, cos, sin) on
+ * q and on k at position_ids; [ds4] Trace 2).
+ *   x          device, f16 [n, t, h, d], rotated in place
+ *   positions  device, int32 [n, t]
+ * Each rotated value is computed in fp64 and rounded to f16 (nearest, ties to even). */
+int attn_rope_apply(void *x, const int32_t *positions, int n, int t, int h, int d,
+                    const kvrope_rope_params *rp, void *stream);
+
+/* kv_cache_append -- copy new rows into the caches ([Sophgo] Listing 2 Concat(history,
+ * new); [Buddy] sec. 6.4.5): cache_k[u, g, lens[u] + i, :] = k[u, i, g, :] and the same
+ * for v, for i < t.  Bit copy; every other row is untouched.
+ *   lens      device, int32 [n], history rows per unit; the host checks
+ *             max_len + t <= s_cap with the caller's bound max_len >= every lens[u]. */
+int kv_cache_append(void *cache_k, void *cache_v, const void *k, const void *v,
+                    const int32_t *lens, int max_len, int n, int t, int hkv, int d, int s_cap,
+                    void *stream);
+
+/* attn_prefill -- a block without history ([Sophgo] Listing 1, sec. 4.1 prefill): the
+ * same as attn_prefill_kv with every history length 0 (hist_lens may be NULL here). */
+int attn_prefill(const void *q, const void *k, const void *v, const int32_t *positions,
+                 void *cache_k, void *cache_v, void *out, int n, int t, int hq, int hkv, int d,
+                 int s_cap, double scale, const kvrope_rope_params *rp, void *stream);
+
+/* attn_prefill_kv -- chunked prefill over a history ([Sophgo] Listing 2, sec. 4.1).
+ *   history_k, history_v  device, f16 [n, hkv, s_cap, d]: the per-unit caches.  Rows
+ *             [0, hist_lens[u]) hold already-rotated history and are read only.
+ *   hist_lens device, int32 [n]; max_hist >= every hist_lens[u] (host bound).
+ * Steps: k is rotated at `positions` (fp64, rounded to f16) and written with v to rows
+ * [hist_lens[u], hist_lens[u] + t); then new token i of unit u and query head h attends
+ * over rows 0 .. hist_lens[u] + i of KV head h / (hq / hkv):
+ *     out = softmax(scale * q_hat K^T) V,
+ * where q_hat is q rotated at `positions` and rounded to f16.  The scores and the softmax
+ * are fp32; out is rounded to f16.  Requires max_hist + t <= s_cap. */
+int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *positions,
+                    void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
+                    void *out, int n, int t, int hq, int hkv, int d, int s_cap, double scale,
+                    const kvrope_rope_params *rp, void *stream);
+
+/* attn_decode -- one new token per unit ([Sophgo] sec. 4.1 decode; [Buddy] sec.
+ * 6.4.5-6.4.6).
+ *   q    [n, 1, hq, d] (= [n, hq, d]);  k, v  [n, 1, hkv, d];  positions [n]
+ *   cache_lens  device, int32 [n]: rows already in the cache; max_len >= every one.
+ *   workspace   device scratch of at least kvrope_workspace_size(KVROPE_OP_DECODE, n, 1,
+ *               hq, hkv, d, max_len) bytes (may be NULL when that size is 0).  Its
+ *               contents on entry do not matter; calls sharing one workspace must be
+ *               ordered on one stream.
+ * Steps: q and k are rotated at positions[u] (k in fp64, both rounded to f16); the new
+ * k, v are written to row cache_lens[u]; then every query head attends over rows
+ * 0 .. cache_lens[u] (cache_lens[u] + 1 keys), split into key chunks whose partial
+ * softmax states are merged in a fixed order (deterministic).  The caller advances its
+ * lengths; the library never writes them.  Requires max_len + 1 <= s_cap. */
+int attn_decode(const void *q, const void *k, const void *v, const int32_t *positions,
+                void *cache_k, void *cache_v, const int32_t *cache_lens, int max_len,
+                void *out, int n, int hq, int hkv, int d, int s_cap, double scale,
+                const kvrope_rope_params *rp, void *workspace, size_t ws_bytes,
+                void *stream);
+
+#define KVROPE_OP_DECODE 1
+
+/* Bytes of device workspace the operation needs (0 for operations that need none). */
+size_t kvrope_workspace_size(int op, int n, int t, int hq, int hkv, int d, int max_len);
+
+/* Static description of a status code (never NULL). */
+const char *kvrope_status_string(int status);
+
+/* The hipError_t of the most recent KVROPE_ERR_HIP on this thread (0 if none). */
+int kvrope_last_hip_error(void);
+
+/* Profiling hook.  When `before` / `after` are non-NULL hipEvent_t handles, the next
+ * attn_prefill, attn_prefill_kv or attn_decode call records `before` on its stream just
+ * before its attention kernel (the flash kernel of prefill, the split-key kernel of
+ * decode) and `after` just after that same kernel, then clears the hook.  One hook per
+ * process; not thread-safe.  Returns KVROPE_OK. */
+int kvrope_set_profile_events(void *before, void *after);
+
+/* The fp64 -> f16 (nearest, ties to even) conversion the kernels apply to every rotated
+ * value, compiled for the host: lets a CPU-only test check it on any input. */
+uint16_t kvrope_f64_to_f16(double x);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVROPE_H */

@@ -1,0 +1,280 @@
+// api.hip -- the C ABI of libkvrope: host-side validation, rotary tables and dispatch.
+//
+// Every status except KVROPE_ERR_HIP is decided here, on the host, before any HIP call.
+// See include/kvrope.h for the contract of each entry point.
+#include "../../include/kvrope.h"
+
+#include "device_common.h"
+#include "launch.h"
+
+#include <math.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+hipEvent_t g_ev_before = nullptr;
+hipEvent_t g_ev_after = nullptr;
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline bool finite_pos(double x) { return isfinite(x) && x > 0.0; }
+
+int check_rope(const kvrope_rope_params *rp, int d)
+{
+    if (!rp)
+        return KVROPE_ERR_NULL;
+    if (rp->n_rot < 2 || rp->n_rot > d || (rp->n_rot & 1))
+        return KVROPE_ERR_ROPE;
+    if (!isfinite(rp->base) || rp->base <= 1.0)
+        return KVROPE_ERR_ROPE;
+    if (!finite_pos(rp->mscale))
+        return KVROPE_ERR_ROPE;
+    if (rp->yarn != 0 && rp->yarn != 1)
+        return KVROPE_ERR_ROPE;
+    if (rp->yarn) {
+        if (!finite_pos(rp->freq_scale) || !isfinite(rp->ext_factor) || rp->ext_factor < 0.0 ||
+            rp->ext_factor > 1.0 || rp->n_ctx_orig <= 0 || !finite_pos(rp->beta_fast) ||
+            !finite_pos(rp->beta_slow))
+            return KVROPE_ERR_ROPE;
+    }
+    return KVROPE_OK;
+}
+
+// Rotary table in fp64 ("ds4.c study notes", Part 4 sec. 1, Traces 1-2): base frequency
+// base^(-2j / n_rot) for pair j; under YaRN it is mixed with the interpolated frequency
+// freq_scale * base^(-2j / n_rot) by the ramp weight
+// g_j = ext_factor * ramp(c(beta_fast), c(beta_slow), j), where the correction dim
+// c(beta) = n_rot * ln(n_ctx_orig / (2 pi beta)) / (2 ln base) and ramp is 1 below its
+// low end, 0 above its high end and linear between (denominator floored at 0.001).
+kvrope::RopeTable rope_table(const kvrope_rope_params &rp, int d)
+{
+    kvrope::RopeTable tab;
+    tab.n_pairs = rp.n_rot / 2;
+    tab.off = d - rp.n_rot;
+    tab.mscale = rp.mscale;
+    const double two_pi = 6.283185307179586476925286766559;
+    double lo = 0.0, hi = 0.0;
+    if (rp.yarn) {
+        const double ln_base = log(rp.base);
+        lo = (double)rp.n_rot * log((double)rp.n_ctx_orig / (two_pi * rp.beta_fast)) / (2.0 * ln_base);
+        hi = (double)rp.n_rot * log((double)rp.n_ctx_orig / (two_pi * rp.beta_slow)) / (2.0 * ln_base);
+    }
+    for (int j = 0; j < kvrope::kMaxPairs; ++j) {
+        double w = 0.0;
+        if (j < tab.n_pairs) {
+            w = pow(rp.base, -2.0 * (double)j / (double)rp.n_rot);
+            if (rp.yarn) {
+                double y = ((double)j - lo) / fmax(0.001, hi - lo);
+                y = y < 0.0 ? 0.0 : (y > 1.0 ? 1.0 : y);
+                const double gamma = rp.ext_factor * (1.0 - y);
+                w = w * (rp.freq_scale * (1.0 - gamma) + gamma);
+            }
+        }
+        tab.w[j] = w;
+        tab.wrev[j] = w / two_pi;
+    }
+    return tab;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return KVROPE_OK;
+    g_last_hip_error = (int)e;
+    return KVROPE_ERR_HIP;
+}
+
+void take_profile_events(hipEvent_t *before, hipEvent_t *after)
+{
+    *before = g_ev_before;
+    *after = g_ev_after;
+    g_ev_before = nullptr;
+    g_ev_after = nullptr;
+}
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+} // namespace
+
+extern "C" {
+
+const char *kvrope_status_string(int status)
+{
+    switch (status) {
+    case KVROPE_OK:
+        return "ok";
+    case KVROPE_ERR_NULL:
+        return "a required pointer is NULL";
+    case KVROPE_ERR_SHAPE:
+        return "invalid shape (negative size, d != 128, hq not a multiple of hkv, or grid too large)";
+    case KVROPE_ERR_ROPE:
+        return "invalid rotary parameters";
+    case KVROPE_ERR_CAPACITY:
+        return "cache capacity exceeded (max_len + t > s_cap) or negative max_len";
+    case KVROPE_ERR_ALIGN:
+        return "a tensor pointer is not 16-byte aligned (int32 arrays: 4-byte)";
+    case KVROPE_ERR_WORKSPACE:
+        return "workspace missing or smaller than kvrope_workspace_size()";
+    case KVROPE_ERR_SCALE:
+        return "softmax scale is not finite and positive";
+    case KVROPE_ERR_HIP:
+        return "a HIP launch failed";
+    default:
+        return "unknown status";
+    }
+}
+
+int kvrope_last_hip_error(void) { return g_last_hip_error; }
+
+int kvrope_set_profile_events(void *before, void *after)
+{
+    g_ev_before = reinterpret_cast<hipEvent_t>(before);
+    g_ev_after = reinterpret_cast<hipEvent_t>(after);
+    return KVROPE_OK;
+}
+
+uint16_t kvrope_f64_to_f16(double x) { return kvrope::f64_to_f16_rne(x); }
+
+size_t kvrope_workspace_size(int op, int n, int t, int hq, int hkv, int d, int max_len)
+{
+    (void)t;
+    (void)d;
+    if (op != KVROPE_OP_DECODE || n <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_len < 0)
+        return 0;
+    return kvrope::decode_workspace_bytes(n, hq, hkv, max_len);
+}
+
+int attn_rope_apply(void *x, const int32_t *positions, int n, int t, int h, int d,
+                    const kvrope_rope_params *rp, void *stream)
+{
+    if (n < 0 || t < 0 || h < 1 || d != kvrope::kHeadDim)
+        return KVROPE_ERR_SHAPE;
+    int st = check_rope(rp, d);
+    if (st)
+        return st;
+    const int64_t rows = (int64_t)n * t;
+    if (rows == 0)
+        return KVROPE_OK;
+    if (!x || !positions)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(x) || !aligned4(positions))
+        return KVROPE_ERR_ALIGN;
+    if (rows * 16 / 256 > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    const kvrope::RopeTable tab = rope_table(*rp, d);
+    return hip_status(kvrope::launch_rope_inplace(static_cast<uint16_t *>(x), positions, rows, h, tab,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int kv_cache_append(void *cache_k, void *cache_v, const void *k, const void *v,
+                    const int32_t *lens, int max_len, int n, int t, int hkv, int d, int s_cap,
+                    void *stream)
+{
+    if (n < 0 || t < 0 || hkv < 1 || d != kvrope::kHeadDim || s_cap < 1)
+        return KVROPE_ERR_SHAPE;
+    if (max_len < 0 || (int64_t)max_len + t > s_cap)
+        return KVROPE_ERR_CAPACITY;
+    if ((int64_t)n * t == 0)
+        return KVROPE_OK;
+    if (!cache_k || !cache_v || !k || !v || !lens)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(cache_k) || !aligned16(cache_v) || !aligned16(k) || !aligned16(v) || !aligned4(lens))
+        return KVROPE_ERR_ALIGN;
+    if ((int64_t)n * t * hkv * 16 / 256 > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    return hip_status(kvrope::launch_append(static_cast<uint16_t *>(cache_k), static_cast<uint16_t *>(cache_v),
+                                            static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
+                                            lens, max_len, n, t, hkv, s_cap, static_cast<hipStream_t>(stream)));
+}
+
+int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *positions,
+                    void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
+                    void *out, int n, int t, int hq, int hkv, int d, int s_cap, double scale,
+                    const kvrope_rope_params *rp, void *stream)
+{
+    if (n < 0 || t < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || d != kvrope::kHeadDim || s_cap < 1)
+        return KVROPE_ERR_SHAPE;
+    int st = check_rope(rp, d);
+    if (st)
+        return st;
+    if (!(isfinite(scale) && scale > 0.0))
+        return KVROPE_ERR_SCALE;
+    if (max_hist < 0 || (int64_t)max_hist + t > s_cap)
+        return KVROPE_ERR_CAPACITY;
+    if ((int64_t)n * t == 0)
+        return KVROPE_OK;
+    if (!q || !k || !v || !positions || !history_k || !history_v || !out)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(history_k) ||
+        !aligned16(history_v) || !aligned16(out) || !aligned4(positions) ||
+        (hist_lens && !aligned4(hist_lens)))
+        return KVROPE_ERR_ALIGN;
+    const int G = hq / hkv;
+    if ((int64_t)n * hkv * G * ((t + 31) / 32) > kMaxGrid || (int64_t)n * t * 16 / 256 > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    const kvrope::RopeTable tab = rope_table(*rp, d);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t eb, ea;
+    take_profile_events(&eb, &ea);
+    uint16_t *ck = static_cast<uint16_t *>(history_k);
+    uint16_t *cv = static_cast<uint16_t *>(history_v);
+    hipError_t e = kvrope::launch_rope_append(ck, cv, static_cast<const uint16_t *>(k),
+                                              static_cast<const uint16_t *>(v), positions, hist_lens,
+                                              max_hist, n, t, hkv, s_cap, tab, s);
+    if (e != hipSuccess)
+        return hip_status(e);
+    kvrope::PrefillShape ps{n, t, hq, hkv, s_cap, max_hist, (float)scale};
+    return hip_status(kvrope::launch_prefill_attention(static_cast<const uint16_t *>(q), ck, cv, positions,
+                                                       hist_lens, static_cast<uint16_t *>(out), ps, tab, s,
+                                                       eb, ea));
+}
+
+int attn_prefill(const void *q, const void *k, const void *v, const int32_t *positions,
+                 void *cache_k, void *cache_v, void *out, int n, int t, int hq, int hkv, int d,
+                 int s_cap, double scale, const kvrope_rope_params *rp, void *stream)
+{
+    return attn_prefill_kv(q, k, v, positions, cache_k, cache_v, nullptr, 0, out, n, t, hq, hkv, d,
+                           s_cap, scale, rp, stream);
+}
+
+int attn_decode(const void *q, const void *k, const void *v, const int32_t *positions,
+                void *cache_k, void *cache_v, const int32_t *cache_lens, int max_len,
+                void *out, int n, int hq, int hkv, int d, int s_cap, double scale,
+                const kvrope_rope_params *rp, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (n < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || d != kvrope::kHeadDim || s_cap < 1)
+        return KVROPE_ERR_SHAPE;
+    int st = check_rope(rp, d);
+    if (st)
+        return st;
+    if (!(isfinite(scale) && scale > 0.0))
+        return KVROPE_ERR_SCALE;
+    if (max_len < 0 || (int64_t)max_len + 1 > s_cap)
+        return KVROPE_ERR_CAPACITY;
+    if (n == 0)
+        return KVROPE_OK;
+    if (!q || !k || !v || !positions || !cache_k || !cache_v || !cache_lens || !out)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cache_k) || !aligned16(cache_v) ||
+        !aligned16(out) || !aligned4(positions) || !aligned4(cache_lens))
+        return KVROPE_ERR_ALIGN;
+    const size_t need = kvrope::decode_workspace_bytes(n, hq, hkv, max_len);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return KVROPE_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace))
+        return KVROPE_ERR_ALIGN;
+    const int64_t nsplit_max = (int64_t)max_len / 128 + 1;
+    if ((int64_t)n * hq * nsplit_max > kMaxGrid || (int64_t)n * hq * 64 / 256 > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    const kvrope::RopeTable tab = rope_table(*rp, d);
+    hipEvent_t eb, ea;
+    take_profile_events(&eb, &ea);
+    kvrope::DecodeShape ds{n, hq, hkv, s_cap, max_len, (float)scale};
+    return hip_status(kvrope::launch_decode(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                                            static_cast<const uint16_t *>(v), positions,
+                                            static_cast<uint16_t *>(cache_k), static_cast<uint16_t *>(cache_v),
+                                            cache_lens, static_cast<uint16_t *>(out), ds, tab, workspace,
+                                            static_cast<hipStream_t>(stream), eb, ea));
+}
+
+} // extern "C"

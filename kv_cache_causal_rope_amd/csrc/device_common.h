@@ -1,0 +1,101 @@
+// device_common.h -- types and small helpers shared by the gfx950 kernels of libkvrope.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvrope {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxPairs = kHeadDim / 2;
+
+// Per-call rotary table, passed by value as a kernel argument.  Built on the host in
+// fp64 (rope_table() in api.cpp): pair j of a head rotates dims (off + 2j, off + 2j + 1)
+// by theta = pos * w[j]; wrev[j] = w[j] / (2 pi) serves the fp32 path that works in
+// revolutions.
+struct RopeTable {
+    double w[kMaxPairs];
+    double wrev[kMaxPairs];
+    double mscale;
+    int n_pairs; // n_rot / 2
+    int off;     // first rotated dim (d - n_rot)
+};
+
+// fp64 -> IEEE binary16, round to nearest, ties to even, by bit manipulation.
+// Used for every rotated K value, so the cache holds the correctly rounded f16 of the
+// fp64 rotation (no intermediate fp32 rounding).
+__host__ __device__ inline uint16_t f64_to_f16_rne(double x)
+{
+    union {
+        double d;
+        uint64_t u;
+    } cv;
+    cv.d = x;
+    const uint64_t b = cv.u;
+    const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+    const int ex = (int)((b >> 52) & 0x7ff);
+    const uint64_t man = b & 0xFFFFFFFFFFFFFull;
+    if (ex == 0x7ff)
+        return (uint16_t)(sign | (man ? 0x7e00u : 0x7c00u));
+    const int e = ex - 1023;
+    if (e > 15)
+        return (uint16_t)(sign | 0x7c00u);
+    if (e >= -14) {
+        uint32_t m16 = (uint32_t)(man >> 42) | 0x400u;
+        const uint64_t rem = man & ((1ull << 42) - 1);
+        const uint64_t half = 1ull << 41;
+        if (rem > half || (rem == half && (m16 & 1u)))
+            ++m16;
+        int eb = e + 15;
+        if (m16 == 0x800u) {
+            m16 = 0x400u;
+            ++eb;
+        }
+        if (eb >= 31)
+            return (uint16_t)(sign | 0x7c00u);
+        return (uint16_t)(sign | (uint32_t)(eb << 10) | (m16 & 0x3ffu));
+    }
+    if (ex == 0 || e < -25)
+        return sign; // below half of the smallest subnormal (2^-25 itself ties to 0)
+    const uint64_t M = man | (1ull << 52);
+    const int shift = 28 - e; // 43 .. 53: value in units of 2^-24
+    uint64_t qv = M >> shift;
+    const uint64_t rem = M & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (qv & 1u)))
+        ++qv;
+    return (uint16_t)(sign | (uint16_t)qv);
+}
+
+__device__ inline float h2f(uint16_t h)
+{
+    union {
+        uint16_t u;
+        _Float16 f;
+    } cv;
+    cv.u = h;
+    return (float)cv.f;
+}
+
+__device__ inline double h2d(uint16_t h) { return (double)h2f(h); }
+
+// fp32 -> f16 with the hardware conversion (round to nearest even in the default mode).
+__device__ inline uint16_t f2h(float x)
+{
+    union {
+        uint16_t u;
+        _Float16 f;
+    } cv;
+    cv.f = (_Float16)x;
+    return cv.u;
+}
+
+__device__ inline uint16_t qnan16() { return 0x7e00u; }
+
+} // namespace kvrope

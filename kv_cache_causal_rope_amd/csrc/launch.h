@@ -1,0 +1,52 @@
+// launch.h -- internal launchers of libkvrope (host side of each kernel file).
+// All sizes were validated by api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvrope {
+
+struct RopeTable;
+
+hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int h,
+                               const RopeTable &tab, hipStream_t stream);
+
+hipError_t launch_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,
+                         const uint16_t *v, const int32_t *lens, int max_len, int n, int t,
+                         int hkv, int s_cap, hipStream_t stream);
+
+hipError_t launch_rope_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,
+                              const uint16_t *v, const int32_t *positions, const int32_t *lens,
+                              int max_len, int n, int t, int hkv, int s_cap,
+                              const RopeTable &tab, hipStream_t stream);
+
+struct PrefillShape {
+    int n, t, hq, hkv, s_cap, max_hist;
+    float scale;
+};
+
+// Causal GQA flash attention over the caches (rows already appended), with q rotated in
+// the kernel's prologue.  lens may be NULL (all zero).
+hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
+                                    const uint16_t *cache_v, const int32_t *positions,
+                                    const int32_t *lens, uint16_t *out, const PrefillShape &s,
+                                    const RopeTable &tab, hipStream_t stream,
+                                    hipEvent_t ev_before, hipEvent_t ev_after);
+
+struct DecodeShape {
+    int n, hq, hkv, s_cap, max_len;
+    float scale;
+};
+
+// Bytes of fp32 workspace the split-key decode needs for this shape.
+size_t decode_workspace_bytes(int n, int hq, int hkv, int max_len);
+
+hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const int32_t *positions, uint16_t *cache_k, uint16_t *cache_v,
+                         const int32_t *lens, uint16_t *out, const DecodeShape &s,
+                         const RopeTable &tab, void *workspace, hipStream_t stream,
+                         hipEvent_t ev_before, hipEvent_t ev_after);
+
+} // namespace kvrope

@@ -1,0 +1,201 @@
+// rope_append.hip -- rotary embedding and KV-cache append kernels (gfx950).
+//
+// Rotation ("ds4.c study notes", Part 4 sec. 1, Trace 2): pair j of a head holds dims
+// (off + 2j, off + 2j + 1), off = d - n_rot; with theta = pos * w[j] and
+// c = cos(theta) * mscale, s = sin(theta) * mscale the pair (x0, x1) becomes
+// (x0 c - x1 s, x0 s + x1 c).  These kernels evaluate it in fp64 and round once to f16
+// (nearest even), so a rotated K row in the cache is the correctly rounded f16 of the
+// exact rotation.
+//
+// Append (Sophgo MLIR-based LLM compilation paper, sec. 3.1 Listing 2: Concat(history,
+// new); Buddy-MLIR walkthrough, sec. 6.4.5): new row i of unit u goes to cache row
+// lens[u] + i of its KV head.  Every kernel here moves 16-byte chunks so that a wave's
+// accesses to one row are contiguous.
+#include "device_common.h"
+#include "launch.h"
+
+namespace kvrope {
+
+namespace {
+
+// Rotate the rotated-region pairs inside one 8-dim chunk (dims 8c .. 8c+7) in fp64.
+// cs/sn hold cos/sin * mscale for the chunk's four candidate pairs (unused where a
+// dim pair lies before `off`).
+__device__ inline void rotate_chunk_f64(const uint16_t (&in)[8], uint16_t (&out)[8], int c,
+                                        const double (&cs)[4], const double (&sn)[4], int off)
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int dim = 8 * c + 2 * m;
+        if (dim >= off) {
+            const double x0 = h2d(in[2 * m]);
+            const double x1 = h2d(in[2 * m + 1]);
+            const double y0 = x0 * cs[m] - x1 * sn[m];
+            const double y1 = x0 * sn[m] + x1 * cs[m];
+            out[2 * m] = f64_to_f16_rne(y0);
+            out[2 * m + 1] = f64_to_f16_rne(y1);
+        } else {
+            out[2 * m] = in[2 * m];
+            out[2 * m + 1] = in[2 * m + 1];
+        }
+    }
+}
+
+__device__ inline void chunk_trig(int c, double pos, const RopeTable &tab, double (&cs)[4],
+                                  double (&sn)[4])
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int dim = 8 * c + 2 * m;
+        cs[m] = 1.0;
+        sn[m] = 0.0;
+        if (dim >= tab.off) {
+            const int j = (dim - tab.off) >> 1;
+            const double theta = pos * tab.w[j];
+            double s, co;
+            sincos(theta, &s, &co);
+            cs[m] = co * tab.mscale;
+            sn[m] = s * tab.mscale;
+        }
+    }
+}
+
+union Chunk16 {
+    uint4 v;
+    uint16_t h[8];
+};
+
+// x[rows, h, 128] rotated in place; one thread per (row, 16-byte chunk of the rotated
+// region), looping over the heads so the trig is shared by all heads of a row.
+__global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict__ x,
+                                                           const int32_t *__restrict__ positions,
+                                                           int64_t rows, int h, RopeTable tab)
+{
+    const int first_chunk = tab.off >> 3;
+    const int nchunks = (kHeadDim >> 3) - first_chunk;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * nchunks)
+        return;
+    const int c = first_chunk + (int)(idx % nchunks);
+    const int64_t r = idx / nchunks;
+    double cs[4], sn[4];
+    chunk_trig(c, (double)positions[r], tab, cs, sn);
+    for (int hh = 0; hh < h; ++hh) {
+        uint4 *p = reinterpret_cast<uint4 *>(x + (r * h + hh) * kHeadDim) + c;
+        Chunk16 in, out;
+        in.v = *p;
+        rotate_chunk_f64(in.h, out.h, c, cs, sn, tab.off);
+        *p = out.v;
+    }
+}
+
+// Pure copy of new rows into the caches: one thread per 16-byte chunk of k (and v).
+__global__ void __launch_bounds__(256) append_kernel(uint16_t *__restrict__ cache_k,
+                                                     uint16_t *__restrict__ cache_v,
+                                                     const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v,
+                                                     const int32_t *__restrict__ lens,
+                                                     int max_len, int n, int t, int hkv,
+                                                     int s_cap)
+{
+    const int64_t total = (int64_t)n * t * hkv * 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int c = (int)(idx & 15);
+    int64_t rest = idx >> 4;
+    const int g = (int)(rest % hkv);
+    rest /= hkv;
+    const int i = (int)(rest % t);
+    const int u = (int)(rest / t);
+    const int len = lens[u];
+    if (len < 0 || len > max_len)
+        return; // host bound violated: leave the cache untouched
+    const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
+    const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
+    reinterpret_cast<uint4 *>(cache_k + dst)[c] = reinterpret_cast<const uint4 *>(k + src)[c];
+    reinterpret_cast<uint4 *>(cache_v + dst)[c] = reinterpret_cast<const uint4 *>(v + src)[c];
+}
+
+// Fused prefill step 1: rotate new k (fp64 -> f16 RNE) and write k, v to cache rows
+// [lens[u], lens[u] + t).  One thread per (unit, token, 16-byte chunk), looping over
+// the KV heads so the trig of a (token, pair) is computed once.
+__global__ void __launch_bounds__(256) rope_append_kernel(
+    uint16_t *__restrict__ cache_k, uint16_t *__restrict__ cache_v,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ positions, const int32_t *__restrict__ lens, int max_len, int n,
+    int t, int hkv, int s_cap, RopeTable tab)
+{
+    const int64_t total = (int64_t)n * t * 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total)
+        return;
+    const int c = (int)(idx & 15);
+    const int64_t ti = idx >> 4;
+    const int i = (int)(ti % t);
+    const int u = (int)(ti / t);
+    const int len = lens ? lens[u] : 0;
+    if (len < 0 || len > max_len)
+        return;
+    double cs[4], sn[4];
+    const bool rotated = 8 * c + 7 >= tab.off;
+    if (rotated)
+        chunk_trig(c, (double)positions[ti], tab, cs, sn);
+    for (int g = 0; g < hkv; ++g) {
+        const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
+        const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
+        Chunk16 in, out;
+        in.v = reinterpret_cast<const uint4 *>(k + src)[c];
+        if (rotated)
+            rotate_chunk_f64(in.h, out.h, c, cs, sn, tab.off);
+        else
+            out.v = in.v;
+        reinterpret_cast<uint4 *>(cache_k + dst)[c] = out.v;
+        reinterpret_cast<uint4 *>(cache_v + dst)[c] = reinterpret_cast<const uint4 *>(v + src)[c];
+    }
+}
+
+inline unsigned grid_for(int64_t threads, int block) { return (unsigned)((threads + block - 1) / block); }
+
+} // namespace
+
+hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int h,
+                               const RopeTable &tab, hipStream_t stream)
+{
+    const int nchunks = (kHeadDim >> 3) - (tab.off >> 3);
+    const int64_t threads = rows * nchunks;
+    if (threads == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(rope_inplace_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
+                       x, positions, rows, h, tab);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,
+                         const uint16_t *v, const int32_t *lens, int max_len, int n, int t,
+                         int hkv, int s_cap, hipStream_t stream)
+{
+    const int64_t threads = (int64_t)n * t * hkv * 16;
+    if (threads == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(append_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
+                       cache_k, cache_v, k, v, lens, max_len, n, t, hkv, s_cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,
+                              const uint16_t *v, const int32_t *positions, const int32_t *lens,
+                              int max_len, int n, int t, int hkv, int s_cap,
+                              const RopeTable &tab, hipStream_t stream)
+{
+    const int64_t threads = (int64_t)n * t * 16;
+    if (threads == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(rope_append_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
+                       cache_k, cache_v, k, v, positions, lens, max_len, n, t, hkv, s_cap, tab);
+    return hipGetLastError();
+}
+
+} // namespace kvrope

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every function include/kvrope.h declares, and every
+host-decided status must come back before any HIP call -- these tests pass fake but
+aligned device pointers, which the library never dereferences on the host.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvrope.h")
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import kv_cache_causal_rope_amd as kv
+    if not os.path.exists(kv.LIB_PATH):
+        from kv_cache_causal_rope_amd import build
+        build.build()
+    kv.lib()
+    return kv
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared_functions()
+    for ep in ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
+               "attn_decode"]:
+        assert ep in names
+
+
+def test_library_exports_every_declared_symbol(kv):
+    out = subprocess.run(["nm", "-D", "--defined-only", kv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    declared = _declared_functions()
+    missing = [n for n in declared if n not in exported]
+    assert not missing, missing
+    assert sorted(kv.EXPORTS) == declared
+
+
+def test_single_hip_runtime_in_process(kv):
+    assert kv._count_hip_runtimes() <= 1
+
+
+# fake, 16-byte aligned "device" pointers: never dereferenced on the host
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+UNALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _prefill_kv(kv, **over):
+    args = dict(q=A, k=A, v=A, pos=A, hk=B, hv=B, hl=A, max_hist=10, out=B, n=2, t=4, hq=12,
+                hkv=2, d=128, s_cap=20, scale=0.088, rp=kv.RopeParams.plain(), stream=None)
+    args.update(over)
+    rp = args["rp"]
+    return kv.lib().attn_prefill_kv(args["q"], args["k"], args["v"], args["pos"], args["hk"],
+                                    args["hv"], args["hl"], args["max_hist"], args["out"],
+                                    args["n"], args["t"], args["hq"], args["hkv"], args["d"],
+                                    args["s_cap"], args["scale"],
+                                    ctypes.byref(rp) if rp is not None else None, args["stream"])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(d=64), -2), (dict(hq=7), -2), (dict(hkv=0), -2), (dict(n=-1), -2),
+    (dict(s_cap=0), -2),
+    (dict(q=None), -1), (dict(out=None), -1), (dict(hk=None), -1), (dict(rp=None), -1),
+    (dict(q=UNALIGNED), -5), (dict(hv=UNALIGNED), -5),
+    (dict(max_hist=17), -4), (dict(max_hist=-1), -4),
+    (dict(scale=0.0), -7), (dict(scale=float("nan")), -7), (dict(scale=float("inf")), -7),
+])
+def test_prefill_kv_host_validation(kv, over, expect):
+    assert _prefill_kv(kv, **over) == expect
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_rot", 3), ("n_rot", 0), ("n_rot", 130), ("base", 1.0), ("base", float("nan")),
+    ("mscale", 0.0), ("yarn", 2),
+])
+def test_rope_parameter_validation(kv, field, value):
+    rp = kv.RopeParams.plain()
+    setattr(rp, field, value)
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ROPE
+
+
+@pytest.mark.parametrize("field,value", [
+    ("freq_scale", 0.0), ("ext_factor", 1.5), ("n_ctx_orig", 0), ("beta_fast", -1.0),
+    ("beta_slow", float("inf")),
+])
+def test_yarn_parameter_validation(kv, field, value):
+    rp = kv.RopeParams.yarn_tail()
+    setattr(rp, field, value)
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ROPE
+
+
+def test_zero_sized_calls_are_noops(kv):
+    assert _prefill_kv(kv, n=0) == 0
+    assert _prefill_kv(kv, t=0) == 0
+    L = kv.lib()
+    assert L.attn_prefill(None, None, None, None, None, None, None, 0, 5, 12, 2, 128, 8, 0.1,
+                          ctypes.byref(kv.RopeParams.plain()), None) == 0
+
+
+def test_prefill_without_history_checks_capacity(kv):
+    L = kv.lib()
+    rp = kv.RopeParams.plain()
+    assert L.attn_prefill(A, A, A, A, B, B, B, 1, 9, 12, 2, 128, 8, 0.1, ctypes.byref(rp), None) == -4
+
+
+def test_decode_validation_and_workspace(kv):
+    L = kv.lib()
+    rp = kv.RopeParams.plain()
+    n, hq, hkv, max_len, s_cap = 28, 12, 2, 1024, 1025
+    need = kv.workspace_size(n, hq, hkv, max_len)
+    assert need > 0 and need % 4 == 0
+
+    def call(ws=A, ws_bytes=need, max_len=max_len, s_cap=s_cap, hq=hq, lens=A):
+        return L.attn_decode(A, A, A, A, B, B, lens, max_len, B, n, hq, hkv, 128, s_cap, 0.088,
+                             ctypes.byref(rp), ws, ws_bytes, None)
+
+    assert call(ws=None) == kv.KVROPE_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == kv.KVROPE_ERR_WORKSPACE
+    assert call(ws=UNALIGNED) == kv.KVROPE_ERR_ALIGN
+    assert call(s_cap=1024) == kv.KVROPE_ERR_CAPACITY
+    assert call(hq=13) == kv.KVROPE_ERR_SHAPE
+    assert call(lens=None) == kv.KVROPE_ERR_NULL
+    assert L.kvrope_workspace_size(kv.KVROPE_OP_DECODE, n, 1, 13, 2, 128, 10) == 0
+
+
+def test_append_and_rope_validation(kv):
+    L = kv.lib()
+    rp = kv.RopeParams.plain()
+    assert L.kv_cache_append(B, B, A, A, A, 5, 2, 4, 2, 128, 8, None) == kv.KVROPE_ERR_CAPACITY
+    assert L.kv_cache_append(B, B, A, A, None, 4, 2, 4, 2, 128, 8, None) == kv.KVROPE_ERR_NULL
+    assert L.kv_cache_append(B, B, UNALIGNED, A, A, 4, 2, 4, 2, 128, 8, None) == kv.KVROPE_ERR_ALIGN
+    assert L.kv_cache_append(B, B, A, A, A, 4, 2, 4, 2, 96, 8, None) == kv.KVROPE_ERR_SHAPE
+    assert L.attn_rope_apply(A, A, 2, 3, 4, 120, ctypes.byref(rp), None) == kv.KVROPE_ERR_SHAPE
+    assert L.attn_rope_apply(None, A, 2, 3, 4, 128, ctypes.byref(rp), None) == kv.KVROPE_ERR_NULL
+    assert L.attn_rope_apply(A, A, 0, 3, 4, 128, ctypes.byref(rp), None) == 0
+
+
+def test_status_strings(kv):
+    for code in range(-8, 1):
+        assert kv.status_string(code)
+    assert kv.status_string(-99) == "unknown status"
+
+
+def test_kernel_f16_conversion_on_host(kv):
+    """The fp64 -> f16 conversion the kernels use for rotated K, against numpy."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000), rng.standard_normal(5000) * 1e-5,
+                        rng.standard_normal(5000) * 3e4, [65504.0, 65519.99, 65520.0, 2.0 ** -25,
+                                                          np.nextafter(2.0 ** -25, 1), -0.0, 0.0,
+                                                          np.inf, -np.inf]])
+    # exact midpoints between adjacent f16 values
+    lo = np.arange(0, 0x7bff, 97, dtype=np.uint16)
+    a = lo.view(np.float16).astype(np.float64)
+    b = (lo + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    x = np.concatenate([x, (a + b) / 2, -(a + b) / 2])
+    got = np.array([kv.f64_to_f16_bits(v) for v in x], dtype=np.uint16)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    nan = kv.f64_to_f16_bits(float("nan"))
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0

@@ -1,0 +1,267 @@
+"""GPU parity: every entry point of libkvrope against the CPU oracle on the same seeded
+inputs, at sizes the oracle finishes in seconds that still span several tiles, ragged
+tails and every query-head group size the kernels specialise for.
+
+Bars (see tests/parity.py): outputs within 2e-3 absolute and 1e-2 row-relative of the
+oracle's fp64 result; V rows and untouched cache rows bit-identical; rotated K rows equal
+to the oracle's f16 rounding (boundary cases counted).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_causal_rope_amd import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import kv_cache_causal_rope_amd as kv
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kv.lib()
+    return kv
+
+
+def ora_rope(r: W.Rope) -> oracle.RopeParams:
+    return oracle.RopeParams(base=r.base, n_rot=r.n_rot, yarn=r.yarn, freq_scale=r.freq_scale,
+                             ext_factor=r.ext_factor, n_ctx_orig=r.n_ctx_orig,
+                             beta_fast=r.beta_fast, beta_slow=r.beta_slow, mscale=r.mscale)
+
+
+def custom(n, t, hq, hkv, s_cap, rope=W.PLAIN_128, seed=100):
+    return W.Config("custom", "prefill_kv", n, 1, t, hq, hkv, 128, rope, 0, 0, s_cap, seed, "")
+
+
+def to_dev(inp: W.Inputs) -> W.Inputs:
+    return W.Inputs(*[x.cuda() for x in dataclasses.astuple(inp)])
+
+
+def bits(x):
+    return P.to_np_bits(x)
+
+
+# ------------------------------------------------------------------ rotary embedding
+@pytest.mark.parametrize("rope,h,maxpos", [(W.PLAIN_128, 12, 5000), (W.YARN_TAIL_64, 8, 40000),
+                                           (W.Rope(n_rot=2), 3, 100),
+                                           (W.Rope(n_rot=38, base=500000.0), 5, 70000)])
+def test_rope_apply_matches_oracle(kv, rope, h, maxpos):
+    g = torch.Generator().manual_seed(11)
+    n, t = 3, 37
+    x = torch.randn((n, t, h, 128), generator=g).half()
+    pos = torch.randint(0, maxpos, (n, t), generator=g, dtype=torch.int32)
+    ref_bits, ref64 = oracle.rope(bits(x).reshape(n * t, h, 128), bits_pos(pos), ora_rope(rope))
+    xd = x.cuda()
+    kv.rope_apply(xd, pos.cuda(), kv.RopeParams.from_fields(rope))
+    torch.cuda.synchronize()
+    got = bits(xd).reshape(n * t, h, 128)
+    P.check_k_rows(got, ref_bits, ref64, "rope_apply")
+
+
+def bits_pos(pos):
+    return pos.numpy().reshape(-1).astype(np.int32)
+
+
+def test_cache_append_bit_exact(kv):
+    g = torch.Generator().manual_seed(12)
+    n, t, hkv, s_cap = 3, 5, 2, 16
+    ck = torch.randn((n, hkv, s_cap, 128), generator=g).half()
+    cv = torch.randn((n, hkv, s_cap, 128), generator=g).half()
+    k = torch.randn((n, t, hkv, 128), generator=g).half()
+    v = torch.randn((n, t, hkv, 128), generator=g).half()
+    lens = torch.tensor([0, 7, 11], dtype=torch.int32)
+    rk, rv = bits(ck).copy(), bits(cv).copy()
+    oracle.append(rk, rv, bits(k), bits(v), lens.numpy())
+    ckd, cvd = ck.cuda(), cv.cuda()
+    kv.cache_append(ckd, cvd, k.cuda(), v.cuda(), lens.cuda(), 11)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(ckd), rk) and np.array_equal(bits(cvd), rv)
+
+
+# ------------------------------------------------------------------ prefill / prefill_kv
+def run_prefill_kv(kv, cfg, lens, rope, poison=False, seed=None):
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32), poison_tail=poison, seed=seed)
+    rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    ref_out, ref64, k64 = oracle.prefill_kv(bits(inp.q), bits(inp.k), bits(inp.v),
+                                            inp.positions.numpy(), rk, rv, inp.lens.numpy(),
+                                            cfg.scale, ora_rope(rope))
+    d = to_dev(inp)
+    out = kv.prefill_kv(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens,
+                        int(max(lens)), kv.RopeParams.from_fields(rope), scale=cfg.scale)
+    torch.cuda.synchronize()
+    return inp, d, out, (ref_out, ref64, k64, rk, rv)
+
+
+def check_prefill(d, out, ref, lens, t, what):
+    ref_out, ref64, k64, rk, rv = ref
+    P.check_attention(bits(out), ref64, what)
+    gk, gv = bits(d.cache_k), bits(d.cache_v)
+    assert np.array_equal(gv, rv), f"{what}: V cache differs"
+    # K: rows outside the appended range must be identical; appended rows by the K rule
+    n = gk.shape[0]
+    for u in range(n):
+        new = slice(lens[u], lens[u] + t)
+        untouched = np.ones(gk.shape[2], bool)
+        untouched[new] = False
+        assert np.array_equal(gk[u][:, untouched], rk[u][:, untouched]), \
+            f"{what}: untouched K rows changed"
+        P.check_k_rows(gk[u][:, new], rk[u][:, new], k64[u].transpose(1, 0, 2), what)
+
+
+def test_prefill_tiny_workload(kv):
+    cfg = W.CONFIGS["tiny_prefill_t64"]
+    inp, d, out, ref = run_prefill_kv(kv, cfg, [0], cfg.rope)
+    check_prefill(d, out, ref, [0], cfg.t, cfg.name)
+
+
+@pytest.mark.parametrize("n,t,hq,hkv", [
+    (3, 77, 12, 2),   # G = 6, ragged tail, several tiles
+    (2, 33, 4, 4),    # G = 1
+    (1, 65, 6, 2),    # G = 3
+    (2, 50, 16, 2),   # G = 8
+    (1, 40, 32, 2),   # G = 16: two head slices per workgroup group
+    (2, 1, 12, 2),    # single token
+    (1, 130, 8, 4),   # G = 2
+])
+def test_prefill_shapes(kv, n, t, hq, hkv):
+    cfg = custom(n, t, hq, hkv, t + 3, seed=200 + t)
+    lens = [0] * n
+    inp, d, out, ref = run_prefill_kv(kv, cfg, lens, W.PLAIN_128)
+    check_prefill(d, out, ref, lens, t, f"prefill n{n} t{t} {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("n,t,hq,hkv,lens,rope", [
+    (2, 45, 32, 2, [37, 100], W.PLAIN_128),
+    (3, 64, 12, 2, [0, 64, 130], W.PLAIN_128),
+    (2, 29, 32, 8, [300, 5], W.YARN_TAIL_64),
+    (1, 96, 6, 6, [1000], W.PLAIN_128),
+])
+def test_prefill_kv_shapes(kv, n, t, hq, hkv, lens, rope):
+    cfg = custom(n, t, hq, hkv, max(lens) + t + 5, rope=rope, seed=300 + t)
+    inp, d, out, ref = run_prefill_kv(kv, cfg, lens, rope)
+    check_prefill(d, out, ref, lens, t, f"prefill_kv n{n} t{t} {hq}/{hkv} {lens}")
+
+
+def test_prefill_poisoned_tail_is_never_read(kv):
+    cfg = custom(2, 50, 12, 2, 200, seed=400)
+    lens = [30, 70]
+    inp, d, out, ref = run_prefill_kv(kv, cfg, lens, W.PLAIN_128, poison=True)
+    check_prefill(d, out, ref, lens, 50, "prefill_kv poisoned")
+
+
+# ------------------------------------------------------------------ decode
+def run_decode(kv, n, hq, hkv, lens, s_cap, rope, seed, poison=False):
+    cfg = W.Config("custom", "decode", n, 1, 1, hq, hkv, 128, rope, 0, 0, s_cap, seed, "")
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32), poison_tail=poison)
+    rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    ref_out, ref64, k64 = oracle.decode(bits(inp.q)[:, 0], bits(inp.k)[:, 0], bits(inp.v)[:, 0],
+                                        inp.positions.numpy()[:, 0], rk, rv, inp.lens.numpy(),
+                                        cfg.scale, ora_rope(rope))
+    d = to_dev(inp)
+    out = kv.decode(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, int(max(lens)),
+                    kv.RopeParams.from_fields(rope), scale=cfg.scale)
+    torch.cuda.synchronize()
+    return d, out, (ref_out, ref64, k64, rk, rv)
+
+
+def check_decode(d, out, ref, lens, what):
+    ref_out, ref64, k64, rk, rv = ref
+    P.check_attention(bits(out)[:, 0], ref64, what)
+    gk, gv = bits(d.cache_k), bits(d.cache_v)
+    assert np.array_equal(gv, rv), f"{what}: V cache differs"
+    for u in range(gk.shape[0]):
+        row = lens[u]
+        P.check_k_rows(gk[u][:, row], rk[u][:, row], k64[u], what)
+        others = np.ones(gk.shape[2], bool)
+        others[row] = False
+        assert np.array_equal(gk[u][:, others], rk[u][:, others]), f"{what}: K rows changed"
+
+
+@pytest.mark.parametrize("n,hq,hkv,lens,rope", [
+    (5, 12, 2, [0, 1, 63, 300, 129], W.PLAIN_128),      # G = 6
+    (4, 32, 8, [700, 31, 512, 1], W.YARN_TAIL_64),       # G = 4, YaRN tail
+    (3, 4, 4, [257, 2, 90], W.PLAIN_128),                # G = 1
+    (2, 32, 2, [1500, 333], W.PLAIN_128),                # G = 16: two head slices
+    (2, 6, 2, [4500, 2049], W.PLAIN_128),                # G = 3, multi-chunk
+    (3, 16, 8, [127, 128, 129], W.PLAIN_128),            # G = 2, chunk boundaries
+])
+def test_decode_shapes(kv, n, hq, hkv, lens, rope):
+    d, out, ref = run_decode(kv, n, hq, hkv, lens, max(lens) + 3, rope, seed=500 + n)
+    check_decode(d, out, ref, lens, f"decode {hq}/{hkv} {lens}")
+
+
+def test_decode_poisoned_tail_is_never_read(kv):
+    lens = [10, 200, 77]
+    d, out, ref = run_decode(kv, 3, 12, 2, lens, 400, W.PLAIN_128, seed=600, poison=True)
+    check_decode(d, out, ref, lens, "decode poisoned")
+
+
+# ------------------------------------------------------------------ phase consistency
+def test_gpu_prefill_equals_successive_gpu_decodes(kv):
+    """Prefill of T tokens and T decode steps from an empty cache agree (GPU only)."""
+    n, t, hq, hkv = 2, 40, 12, 2
+    cfg = custom(n, t, hq, hkv, t, seed=700)
+    inp = W.make_inputs(cfg, lens=np.zeros(n, np.int32))
+    d = to_dev(inp)
+    rp = kv.RopeParams.plain()
+    ck1, cv1 = torch.zeros_like(d.cache_k), torch.zeros_like(d.cache_v)
+    out1 = kv.prefill(d.q, d.k, d.v, d.positions, ck1, cv1, rp)
+    ck2, cv2 = torch.zeros_like(d.cache_k), torch.zeros_like(d.cache_v)
+    outs = []
+    for i in range(t):
+        lens = torch.full((n,), i, dtype=torch.int32, device="cuda")
+        outs.append(kv.decode(d.q[:, i:i + 1].contiguous(), d.k[:, i:i + 1].contiguous(),
+                              d.v[:, i:i + 1].contiguous(), d.positions[:, i].contiguous(),
+                              ck2, cv2, lens, i, rp))
+    torch.cuda.synchronize()
+    out2 = torch.cat(outs, dim=1)
+    assert torch.equal(ck1, ck2) and torch.equal(cv1, cv2)
+    diff = (out1.double() - out2.double()).abs().max().item()
+    assert diff <= 2e-3, diff
+
+
+def test_deterministic(kv):
+    cfg = custom(2, 70, 12, 2, 90, seed=800)
+    inp = W.make_inputs(cfg, lens=np.array([3, 10], np.int32))
+    rp = kv.RopeParams.plain()
+    res = []
+    for _ in range(2):
+        d = to_dev(inp)
+        o1 = kv.prefill_kv(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, 10, rp)
+        o2 = kv.decode(d.q[:, :1].contiguous(), d.k[:, :1].contiguous(), d.v[:, :1].contiguous(),
+                       (d.lens + 70).contiguous(), d.cache_k, d.cache_v, (d.lens + 70).contiguous(),
+                       80, rp)
+        torch.cuda.synchronize()
+        res.append((o1.clone(), o2.clone(), d.cache_k.clone()))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+
+
+def test_out_of_range_length_yields_nan_and_no_write(kv):
+    """A device length above the host bound: the kernels skip that unit (no cache write,
+    NaN output) and leave the other units correct."""
+    lens = [5, 9]
+    cfg = W.Config("custom", "decode", 2, 1, 1, 12, 2, 128, W.PLAIN_128, 0, 0, 20, 900, "")
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32))
+    d = to_dev(inp)
+    bad = torch.tensor([5, 15], dtype=torch.int32, device="cuda")   # 15 > max_len = 9
+    ck0 = d.cache_k.clone()
+    out = kv.decode(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, bad, 9, kv.RopeParams.plain())
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
+    assert torch.equal(d.cache_k[1], ck0[1])
+    # prefill_kv
+    cfgp = custom(2, 8, 12, 2, 30, seed=901)
+    inp = W.make_inputs(cfgp, lens=np.array([4, 6], np.int32))
+    d = to_dev(inp)
+    ck0 = d.cache_k.clone()
+    badh = torch.tensor([4, 25], dtype=torch.int32, device="cuda")
+    out = kv.prefill_kv(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, badh, 6,
+                        kv.RopeParams.plain())
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
+    assert torch.equal(d.cache_k[1], ck0[1])
