@@ -11,6 +11,10 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+// Native 16-byte vector (HIP's uint4 is a struct with a union inside, which can keep
+// values out of registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxPairs = kHeadDim / 2;
@@ -73,27 +77,24 @@ __host__ __device__ inline uint16_t f64_to_f16_rne(double x)
     return (uint16_t)(sign | (uint16_t)qv);
 }
 
-__device__ inline float h2f(uint16_t h)
-{
-    union {
-        uint16_t u;
-        _Float16 f;
-    } cv;
-    cv.u = h;
-    return (float)cv.f;
-}
+__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Low / high f16 of a 32-bit word, widened to fp32.
+__device__ inline float lo2f(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
+__device__ inline float hi2f(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+__device__ inline u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ inline void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 __device__ inline double h2d(uint16_t h) { return (double)h2f(h); }
 
 // fp32 -> f16 with the hardware conversion (round to nearest even in the default mode).
-__device__ inline uint16_t f2h(float x)
+__device__ inline uint16_t f2h(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// Two fp32 -> packed f16 pair (each rounded to nearest even), low half first.
+__device__ inline uint32_t pack2h(float a, float b)
 {
-    union {
-        uint16_t u;
-        _Float16 f;
-    } cv;
-    cv.f = (_Float16)x;
-    return cv.u;
+    return (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
 }
 
 __device__ inline uint16_t qnan16() { return 0x7e00u; }

@@ -9,11 +9,12 @@
 // The caches already hold the new rows (rope_append_kernel ran first).  q is rotated
 // in the prologue ("ds4.c study notes", Part 4 sec. 1, Trace 2) and rounded to f16.
 //
-// Work decomposition.  A workgroup owns one (unit, KV head, slice of the head group,
-// block of 32 new tokens); each of its W waves owns one query head of that group and
-// the 32 tokens.  The W waves share every K/V tile the workgroup stages in LDS, so a
-// tile read from L2 feeds W*32 query rows.  Per 64-key tile a wave issues 32 MFMAs
-// (v_mfma_f32_32x32x16_f16):
+// Work decomposition.  For one (unit, KV head) the work items are (block of 32 new
+// tokens, query head of the group), numbered token-block-major.  A workgroup of 8 waves
+// takes 8 consecutive items (one per wave), so it spans at most two adjacent token
+// blocks and shares every K/V tile it stages in LDS among 8 x 32 query rows; 8 waves
+// also keep the 4 SIMDs of a CU evenly loaded for any group size.  Per 64-key tile a
+// wave issues 32 MFMAs (v_mfma_f32_32x32x16_f16):
 //   S^T (64 keys x 32 queries) = K . Q^T        -- 2 key blocks x 8 head-dim steps
 //   O^T (128 dims x 32 queries) += V^T . P^T    -- 2 key blocks x 2 key steps x 4 dim blocks
 // Working on S^T puts one query in each lane (lane l: query l % 32, half l / 32), so the
@@ -21,34 +22,50 @@
 // are already in the B-operand layout of the PV product (the key order inside each
 // 16-key step is permuted consistently on both operands, which the reduction allows).
 // Softmax runs in fp32 in the log2 domain (exp2 of scale*log2(e)-scaled scores) with the
-// usual running max / running sum rescaling.
+// running max / running sum rescaling, applied lazily: the accumulators are rescaled only
+// when some lane's max grows by more than 2^8, so the probabilities stay <= 256 (exact
+// enough in f16) and most tiles skip the 64 multiplies.  The causal mask is applied only
+// on tiles that reach past the first query of the block.
 //
-// LDS (double buffered, one barrier per tile):
-//   K tile: [64 keys][136 halves] (row padding keeps 16-byte reads of 16 consecutive
-//           keys on distinct banks);
-//   V tile: [16 key quads][128 dims][4 keys] with the dim index xor-swizzled inside
-//           groups of 8, so the transposed A-operand reads (4 consecutive keys of one
-//           dim) are contiguous and the transposing writes spread over banks.
-// Grid order: heavier (later) token blocks first; when the number of (unit, KV head)
-// pairs is a multiple of 8, all blocks of one pair go to the same XCD (blocks are dealt
-// to the 8 XCDs round-robin) so its K/V stays in that XCD's L2.
+// LDS (double buffered, one barrier per tile).  K and V tiles go from HBM/L2 straight
+// into LDS (global_load_lds_dwordx4: lane L of a wave's load lands at byte 16 L of a
+// 1 KB LDS block), so staging costs no registers and no VALU; the next tile's loads are
+// issued before the current tile's math.  Both tiles are row-major [64 keys][256 B] with
+// the 16-byte chunk index xor-swizzled by the row:
+//   K: chunk ^ (key & 15)        -- the S^T A-operand reads (16 B of 32 consecutive keys)
+//                                   hit distinct banks;
+//   V: chunk ^ ((key & 3) << 2)  -- the PV A-operand comes from ds_read_b64_tr_b16: in
+//                                   each 16-lane group, lane 4k+m points at 4 dims of
+//                                   key row k and lane i receives dim i of the 4 rows,
+//                                   i.e. 4 consecutive keys of one head dim (V^T).
+// All per-lane LDS addresses are computed once; the tile loop is unrolled by two so
+// both pipeline stages are immediate offsets.
+// Grid order: heavier (later) work first; when the number of (unit, KV head) pairs is a
+// multiple of 8, all workgroups of one pair go to the same XCD (workgroups are dealt to
+// the 8 XCDs round-robin) so its K/V stays in that XCD's L2.
 #include "device_common.h"
 #include "launch.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace kvrope {
 
 namespace {
 
-constexpr int KT = 64;          // keys per tile
-constexpr int QB = 32;          // query tokens per wave
-constexpr int KPITCH = 136;     // halves per K row in LDS
-constexpr int K_STAGE = KT * KPITCH;
-constexpr int V_STAGE = KT * kHeadDim;
-constexpr int STAGE = K_STAGE + V_STAGE; // halves per pipeline stage
-constexpr int LDS_BYTES = 2 * STAGE * 2;
-constexpr int TASKS = KT / 4 * (kHeadDim / 8); // 256 loader tasks: (key quad, 16-byte chunk)
+constexpr int KT = 64;                 // keys per tile
+constexpr int QB = 32;                 // query tokens per wave
+constexpr int NW = 8;                  // waves per workgroup
+constexpr int NT = NW * 64;            // threads per workgroup
+constexpr int ROWB = kHeadDim * 2;     // bytes per K / V row
+constexpr int TILE_B = KT * ROWB;      // 16 KB per tensor per stage
+constexpr int STAGE_B = 2 * TILE_B;    // K tile, then V tile
+constexpr float RESCALE_LOG2 = 8.f;    // lazy-rescale threshold (log2 units)
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) short4v lds_short4_t;
 
 struct PrefillParams {
     const uint16_t *q;
@@ -58,116 +75,73 @@ struct PrefillParams {
     const int32_t *lens;
     uint16_t *out;
     int n, t, hq, hkv, s_cap, max_hist;
-    int W;       // waves (= query heads) per workgroup
-    int slices;  // (hq / hkv) / W
-    int tblocks; // ceil(t / 32)
+    int G;       // query heads per KV head
+    int items;   // tblocks * G work items per (unit, KV head)
+    int wpk;     // workgroups per (unit, KV head) = ceil(items / 8)
     int xcd;     // XCD-aware block mapping
     float scale_log2;
 };
 
-__device__ inline int vswz(int dim) { return dim ^ ((dim >> 3) & 7); }
+__device__ inline int kswz(int key) { return key & 15; }
+__device__ inline int vswz(int key) { return (key & 3) << 2; }
 
-union U4H {
-    uint4 v;
-    uint16_t h[8];
-};
-
-template <int TPT>
-struct TileRegs {
-    uint4 k[TPT][4];
-    uint4 v[TPT][4];
-};
-
-template <int TPT>
-__device__ inline void load_tile(TileRegs<TPT> &r, const uint16_t *kbase, const uint16_t *vbase,
-                                 int kb, int kend, int tid, int nthr)
+// Issue one tile (keys kb .. kb+63, clamped to klast) into an LDS stage: wave w moves 16
+// rows of K (w < 4) or V (w >= 4), 4 rows per instruction.
+__device__ inline void dma_tile(const uint16_t *kbase, const uint16_t *vbase, int kb, int klast,
+                                char *stage, int wave, int lane)
 {
+    const bool isv = wave >= 4;
+    const uint16_t *g = isv ? vbase : kbase;
+    char *tdst = stage + (isv ? TILE_B : 0);
+    const int r0 = 16 * (wave & 3);
 #pragma unroll
-    for (int tt = 0; tt < TPT; ++tt) {
-        const int task = tid + tt * nthr;
-        const int qd = task >> 4, mm = task & 15;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int key = kb + 4 * qd + rr;
-            if (task < TASKS && key < kend) {
-                r.k[tt][rr] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)key * kHeadDim + 8 * mm);
-                r.v[tt][rr] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)key * kHeadDim + 8 * mm);
-            } else {
-                r.k[tt][rr] = make_uint4(0, 0, 0, 0);
-                r.v[tt][rr] = make_uint4(0, 0, 0, 0);
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 4 * i + (lane >> 4);
+        const int gchunk = (lane & 15) ^ (isv ? vswz(row) : kswz(row));
+        const int key = min(kb + row, klast);
+        const uint16_t *src = g + (int64_t)key * kHeadDim + gchunk * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tdst + (r0 + 4 * i) * ROWB), 16, 0, 0);
     }
 }
 
-template <int TPT>
-__device__ inline void store_tile(const TileRegs<TPT> &r, uint16_t *stage, int tid, int nthr)
+__global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab)
 {
-    uint16_t *Ks = stage;
-    uint16_t *Vs = stage + K_STAGE;
-#pragma unroll
-    for (int tt = 0; tt < TPT; ++tt) {
-        const int task = tid + tt * nthr;
-        if (task >= TASKS)
-            continue;
-        const int qd = task >> 4, mm = task & 15;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            *reinterpret_cast<uint4 *>(Ks + (4 * qd + rr) * KPITCH + 8 * mm) = r.k[tt][rr];
-        U4H v0, v1, v2, v3;
-        v0.v = r.v[tt][0];
-        v1.v = r.v[tt][1];
-        v2.v = r.v[tt][2];
-        v3.v = r.v[tt][3];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int slot = vswz(8 * mm + e);
-            uint2 quad;
-            quad.x = (uint32_t)v0.h[e] | ((uint32_t)v1.h[e] << 16);
-            quad.y = (uint32_t)v2.h[e] | ((uint32_t)v3.h[e] << 16);
-            *reinterpret_cast<uint2 *>(Vs + (qd * kHeadDim + slot) * 4) = quad;
-        }
-    }
-}
-
-template <int TPT>
-__global__ void __launch_bounds__(TPT == 1 ? 512 : 256) prefill_attn_kernel(PrefillParams p, RopeTable tab)
-{
-    extern __shared__ __align__(16) uint16_t lds[];
+    // two pipeline stages as separate objects, so the compiler can tell that loads into
+    // one stage never alias reads of the other (no spurious waits on the in-flight tile)
+    __shared__ __align__(16) char lds_st0[STAGE_B];
+    __shared__ __align__(16) char lds_st1[STAGE_B];
+    __shared__ double wrev[kMaxPairs];
 
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int c = lane & 31;  // query within the wave's block (S^T column)
     const int hh = lane >> 5; // lane half
 
-    // ---- block -> (unit, KV head, head slice, token block)
+    // ---- block -> (unit, KV head, workgroup rank); heavier workgroups first
     const int KP = p.n * p.hkv;
-    const int S = p.slices;
-    int kp, sl, tbr;
+    int kp, rank;
     const int b = blockIdx.x;
     if (p.xcd) {
         const int x = b & 7, slot = b >> 3;
-        const int per_rank = (KP >> 3) * S;
-        tbr = slot / per_rank;
-        const int r = slot - tbr * per_rank;
-        kp = x + 8 * (r / S);
-        sl = r % S;
+        const int per_x = KP >> 3;
+        rank = slot / per_x;
+        kp = x + 8 * (slot - rank * per_x);
     } else {
-        const int per_rank = KP * S;
-        tbr = b / per_rank;
-        const int r = b - tbr * per_rank;
-        kp = r / S;
-        sl = r % S;
+        rank = b / KP;
+        kp = b - rank * KP;
     }
-    const int tb = p.tblocks - 1 - tbr;
-    const int u = kp / p.hkv, g = kp - (kp / p.hkv) * p.hkv;
-    const int G = p.hq / p.hkv;
-    const int h = g * G + sl * p.W + wave;
+    const int wk = p.wpk - 1 - rank;
+    const int u = kp / p.hkv, g = kp - u * p.hkv;
+    const int item = wk * NW + wave;
+    const bool wave_valid = item < p.items;
+    const int last_item = min(wk * NW + NW - 1, p.items - 1);
+    const int my_item = wave_valid ? item : last_item;
+    const int tb = my_item / p.G;
+    const int h = g * p.G + (my_item - tb * p.G);
     const int i0 = tb * QB;
     const int i = i0 + c;
-    const bool row_valid = i < p.t;
+    const bool row_valid = wave_valid && i < p.t;
 
     const int hist = p.lens ? p.lens[u] : 0;
     if (hist < 0 || hist > p.max_hist) {
@@ -179,36 +153,47 @@ __global__ void __launch_bounds__(TPT == 1 ? 512 : 256) prefill_attn_kernel(Pref
         }
         return;
     }
-    const int kend = hist + min(i0 + QB, p.t);
+    const int tb_last = last_item / p.G;
+    const int kend = hist + min((tb_last + 1) * QB, p.t); // keys the workgroup needs
     const int ntiles = (kend + KT - 1) / KT;
-    const int qlimit = hist + i; // last visible key of this lane's query
+    const int kend_w = hist + min(i0 + QB, p.t);        // keys this wave needs
+    const int qlimit = hist + i;                         // last visible key of the lane's query
 
     const uint16_t *kbase = p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim;
     const uint16_t *vbase = p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim;
 
-    // ---- issue the first tile's loads before the q prologue
-    TileRegs<TPT> regs;
-    load_tile<TPT>(regs, kbase, vbase, 0, kend, tid, nthr);
+    // ---- first tile and this lane's q row in flight; rotation table to LDS
+    dma_tile(kbase, vbase, 0, kend - 1, lds_st0, wave, lane);
+    // rows past t read row t-1 (branch-free loads; their outputs are never written)
+    const int iq = min(i, p.t - 1);
+    const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
+    const int qpos = p.pos[(int64_t)u * p.t + iq];
+    u32x4 qin[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        qin[s] = ld16(qrow + 16 * s + 8 * hh);
+    if (tid < kMaxPairs)
+        wrev[tid] = tab.wrev[tid];
+    __syncthreads();
 
-    // ---- q prologue: load, rotate (fp32 trig with fp64 range reduction), round to f16
+    // ---- q prologue: rotate (fp32 trig with fp64 range reduction), round to f16
     half8 qop[8];
     {
-        const uint16_t *qrow = p.q + (((int64_t)u * p.t + (row_valid ? i : 0)) * p.hq + h) * kHeadDim;
-        const double posd = row_valid ? (double)p.pos[(int64_t)u * p.t + i] : 0.0;
+        const double posd = (double)qpos;
         const float msc = (float)tab.mscale;
+        const int off = tab.off;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            U4H in;
-            in.v = row_valid ? *reinterpret_cast<const uint4 *>(qrow + 16 * s + 8 * hh)
-                             : make_uint4(0, 0, 0, 0);
-            half8 hv;
+            const u32x4 in = qin[s];
+            u32x4 hv;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int dim = 16 * s + 8 * hh + 2 * m;
-                float x0 = h2f(in.h[2 * m]), x1 = h2f(in.h[2 * m + 1]);
-                if (dim >= tab.off) {
-                    const int j = (dim - tab.off) >> 1;
-                    double rev = posd * tab.wrev[j];
+                const uint32_t w = in[m];
+                float x0 = lo2f(w), x1 = hi2f(w);
+                if (dim >= off) {
+                    const int j = (dim - off) >> 1;
+                    double rev = posd * wrev[j];
                     rev -= floor(rev);
                     const float rf = (float)rev;
                     const float cs = __builtin_amdgcn_cosf(rf) * msc;
@@ -218,14 +203,29 @@ __global__ void __launch_bounds__(TPT == 1 ? 512 : 256) prefill_attn_kernel(Pref
                     x0 = y0;
                     x1 = y1;
                 }
-                hv[2 * m] = (_Float16)x0;
-                hv[2 * m + 1] = (_Float16)x1;
+                hv[m] = pack2h(x0, x1);
             }
-            qop[s] = hv;
+            qop[s] = __builtin_bit_cast(half8, hv);
         }
     }
 
-    store_tile<TPT>(regs, lds, tid, nthr);
+    // ---- per-lane LDS byte addresses inside a stage
+    int kaddr[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        kaddr[s] = c * ROWB + (((2 * s + hh) ^ kswz(c)) << 4);
+    int vaddr[4];
+    {
+        const int grp = lane >> 4, j = lane & 15, kk = j >> 2, m = j & 3;
+        const int row = 4 * (grp >> 1) + kk;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int chunk = 4 * db + 2 * (grp & 1) + (m >> 1);
+            vaddr[db] = TILE_B + row * ROWB + ((chunk ^ vswz(row)) << 4) + 8 * (m & 1);
+        }
+    }
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     floatx16 o[4];
@@ -233,88 +233,109 @@ __global__ void __launch_bounds__(TPT == 1 ? 512 : 256) prefill_attn_kernel(Pref
     for (int db = 0; db < 4; ++db)
         o[db] = floatx16{0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = p.scale_log2;
 
-    for (int tile = 0; tile < ntiles; ++tile) {
+    auto step = [&](auto stg_c, int tile) {
+        constexpr int STG = decltype(stg_c)::value;
+        const char *st = STG ? lds_st1 : lds_st0;
         const int kb = tile * KT;
-        const uint16_t *Ks = lds + (tile & 1) * STAGE;
-        const uint16_t *Vs = Ks + K_STAGE;
-        const bool more = tile + 1 < ntiles;
-        if (more)
-            load_tile<TPT>(regs, kbase, vbase, kb + KT, kend, tid, nthr);
+        if (tile + 1 < ntiles)
+            dma_tile(kbase, vbase, kb + KT, kend - 1, STG ? lds_st0 : lds_st1, wave, lane);
 
-        // S^T = K . Q^T for the tile's two 32-key blocks
-        floatx16 sacc[2];
+        if (wave_valid && kb < kend_w) {
+            // S^T = K . Q^T for the tile's two 32-key blocks
+            floatx16 sacc[2];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            sacc[sb] = floatx16{0.f};
+            for (int sb = 0; sb < 2; ++sb) {
+                half8 kop[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const half8 a = *reinterpret_cast<const half8 *>(Ks + (32 * sb + c) * KPITCH + 16 * s + 8 * hh);
-                sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[s], sacc[sb], 0, 0, 0);
+                for (int s = 0; s < 8; ++s)
+                    kop[s] = *reinterpret_cast<const half8 *>(st + kaddr[s] + sb * 32 * ROWB);
+                sacc[sb] = floatx16{0.f};
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[s], qop[s], sacc[sb], 0, 0, 0);
             }
-        }
 
-        // scale, causal mask, running max
-        const bool need_mask = kb + KT - 1 > hist + i0;
-        float mx = -INFINITY;
+            // causal mask (only on tiles reaching past the block's first query)
+            if (kb + KT - 1 > hist + i0) {
+                const int lim = qlimit - kb - 4 * hh;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+                for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float sv = sacc[sb][r] * p.scale_log2;
-                if (need_mask) {
-                    const int key = kb + 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (key > qlimit)
-                        sv = -INFINITY;
-                }
-                sacc[sb][r] = sv;
-                mx = fmaxf(mx, sv);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float rs = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(sacc[sb][r] - m_new);
-                sacc[sb][r] = pv;
-                rs += pv;
-            }
-        }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            o[db] *= alpha;
-
-        // O^T += V^T . P^T
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                half8 pop;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    pop[j] = (_Float16)sacc[sb][8 * s2 + j];
-                const int q1 = 8 * sb + 4 * s2 + hh;
-                const int q2 = q1 + 2;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const int slot = vswz(32 * db + c);
-                    const half4 lo = *reinterpret_cast<const half4 *>(Vs + (q1 * kHeadDim + slot) * 4);
-                    const half4 hi = *reinterpret_cast<const half4 *>(Vs + (q2 * kHeadDim + slot) * 4);
-                    const half8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pop, o[db], 0, 0, 0);
+                    for (int r = 0; r < 16; ++r) {
+                        if (32 * sb + 8 * (r >> 2) + (r & 3) > lim)
+                            sacc[sb][r] = -INFINITY;
+                    }
                 }
             }
-        }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, sacc[sb][r]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+            if (__any(mx > m_run + RESCALE_LOG2)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    o[db] *= alpha;
+                m_run = m_new;
+            }
+            float rs = 0.f;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][r], sl2, -m_run));
+                    sacc[sb][r] = pv;
+                    rs += pv;
+                }
+            }
+            l_run += rs;
 
-        if (more)
-            store_tile<TPT>(regs, lds + ((tile + 1) & 1) * STAGE, tid, nthr);
+            // O^T += V^T . P^T ; V^T operands by transposing LDS reads
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int rowoff = (32 * sb + 16 * s2) * ROWB;
+                    short4v vlo[4], vhi[4];
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_short4_t *)(st + vaddr[db] + rowoff));
+                        vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_short4_t *)(st + vaddr[db] + rowoff + 8 * ROWB));
+                    }
+                    u32x4 pw;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pw[j] = pack2h(sacc[sb][8 * s2 + 2 * j], sacc[sb][8 * s2 + 2 * j + 1]);
+                    const half8 pop = __builtin_bit_cast(half8, pw);
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        const short4v lo = vlo[db], hi = vhi[db];
+                        const half8 a = __builtin_bit_cast(
+                            half8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                              hi[0], hi[1], hi[2], hi[3]});
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pop, o[db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    for (int tile = 0; tile < ntiles; tile += 2) {
+        step(std::integral_constant<int, 0>{}, tile);
+        if (tile + 1 < ntiles)
+            step(std::integral_constant<int, 1>{}, tile + 1);
     }
 
     // ---- normalise and write: lane holds dims 32db + 8*(r/4) + 4*hh + r%4 of query c
@@ -326,21 +347,12 @@ __global__ void __launch_bounds__(TPT == 1 ? 512 : 256) prefill_attn_kernel(Pref
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
-                uint2 w;
-                w.x = (uint32_t)f2h(o[db][4 * ig + 0] * inv) | ((uint32_t)f2h(o[db][4 * ig + 1] * inv) << 16);
-                w.y = (uint32_t)f2h(o[db][4 * ig + 2] * inv) | ((uint32_t)f2h(o[db][4 * ig + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * ig + 4 * hh) = w;
+                const u32x2 w = {pack2h(o[db][4 * ig + 0] * inv, o[db][4 * ig + 1] * inv),
+                                 pack2h(o[db][4 * ig + 2] * inv, o[db][4 * ig + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * ig + 4 * hh) = w;
             }
         }
     }
-}
-
-int largest_divisor_at_most(int g, int cap)
-{
-    for (int w = cap < g ? cap : g; w >= 1; --w)
-        if (g % w == 0)
-            return w;
-    return 1;
 }
 
 } // namespace
@@ -366,47 +378,18 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
     p.hkv = s.hkv;
     p.s_cap = s.s_cap;
     p.max_hist = s.max_hist;
-    const int G = s.hq / s.hkv;
-    p.W = largest_divisor_at_most(G, 8);
-    p.slices = G / p.W;
-    p.tblocks = (s.t + QB - 1) / QB;
+    p.G = s.hq / s.hkv;
+    const int tblocks = (s.t + QB - 1) / QB;
+    p.items = tblocks * p.G;
+    p.wpk = (p.items + NW - 1) / NW;
     const int KP = s.n * s.hkv;
     p.xcd = (KP % 8 == 0) ? 1 : 0;
     p.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
-    const int64_t blocks = (int64_t)KP * p.slices * p.tblocks;
-    const int threads = 64 * p.W;
-    const int tpt = (TASKS + threads - 1) / threads;
+    const int64_t blocks = (int64_t)KP * p.wpk;
 
     if (ev_before)
         (void)hipEventRecord(ev_before, stream);
-    if (tpt <= 1) {
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_attn_kernel<1>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-            attr = true;
-        }
-        hipLaunchKernelGGL(prefill_attn_kernel<1>, dim3((unsigned)blocks), dim3(threads), LDS_BYTES,
-                           stream, p, tab);
-    } else if (tpt <= 2) {
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_attn_kernel<2>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-            attr = true;
-        }
-        hipLaunchKernelGGL(prefill_attn_kernel<2>, dim3((unsigned)blocks), dim3(threads), LDS_BYTES,
-                           stream, p, tab);
-    } else {
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_attn_kernel<4>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-            attr = true;
-        }
-        hipLaunchKernelGGL(prefill_attn_kernel<4>, dim3((unsigned)blocks), dim3(threads), LDS_BYTES,
-                           stream, p, tab);
-    }
+    hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p, tab);
     hipError_t err = hipGetLastError();
     if (ev_after)
         (void)hipEventRecord(ev_after, stream);
