@@ -11,6 +11,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 // Native 16-byte vector (HIP's uint4 is a struct with a union inside, which can keep
 // values out of registers).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

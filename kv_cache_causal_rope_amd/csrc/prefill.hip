@@ -27,10 +27,12 @@
 // enough in f16) and most tiles skip the 64 multiplies.  The causal mask is applied only
 // on tiles that reach past the first query of the block.
 //
-// LDS (double buffered, one barrier per tile).  K and V tiles go from HBM/L2 straight
+// LDS (four stages).  K and V tiles go from HBM/L2 straight
 // into LDS (global_load_lds_dwordx4: lane L of a wave's load lands at byte 16 L of a
-// 1 KB LDS block), so staging costs no registers and no VALU; the next tile's loads are
-// issued before the current tile's math.  Both tiles are row-major [64 keys][256 B] with
+// 1 KB LDS block), so staging costs no registers and no VALU; each tile's loads are
+// issued two tiles ahead of its first use.  (In each 16-lane group of that load, lanes
+// 16r .. 16r+15 fill row r of the 4-row block: the swizzle picks which global chunk each
+// lane fetches.)  Both tiles are row-major [64 keys][256 B] with
 // the 16-byte chunk index xor-swizzled by the row:
 //   K: chunk ^ (key & 15)        -- the S^T A-operand reads (16 B of 32 consecutive keys)
 //                                   hit distinct banks;
@@ -38,8 +40,10 @@
 //                                   each 16-lane group, lane 4k+m points at 4 dims of
 //                                   key row k and lane i receives dim i of the 4 rows,
 //                                   i.e. 4 consecutive keys of one head dim (V^T).
-// All per-lane LDS addresses are computed once; the tile loop is unrolled by two so
-// both pipeline stages are immediate offsets.
+// All per-lane LDS addresses are computed once; the phase loop is unrolled over the four
+// stages so they are immediate offsets (and separate objects, so loads into one stage
+// never make the compiler wait before reading another), and the operand reads are
+// software-pipelined ahead of the MFMAs that consume them.
 // Grid order: heavier (later) work first; when the number of (unit, KV head) pairs is a
 // multiple of 8, all workgroups of one pair go to the same XCD (workgroups are dealt to
 // the 8 XCDs round-robin) so its K/V stays in that XCD's L2.
@@ -64,7 +68,6 @@ constexpr int STAGE_B = 2 * TILE_B;    // K tile, then V tile
 constexpr float RESCALE_LOG2 = 8.f;    // lazy-rescale threshold (log2 units)
 
 typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) short4v lds_short4_t;
 
 struct PrefillParams {
@@ -82,17 +85,30 @@ struct PrefillParams {
     float scale_log2;
 };
 
+// Workgroup barrier without the release fence of __syncthreads (which would drain every
+// outstanding global load, including tiles prefetched for later phases).  LDS reads and
+// writes complete before it (lgkmcnt); tile loads into LDS are waited for explicitly
+// with vmcnt; the memory clobber keeps the compiler from moving memory ops across it.
+__device__ inline void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline int kswz(int key) { return key & 15; }
 __device__ inline int vswz(int key) { return (key & 3) << 2; }
 
+__device__ inline uint32_t lds_offset(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
 // Issue one tile (keys kb .. kb+63, clamped to klast) into an LDS stage: wave w moves 16
-// rows of K (w < 4) or V (w >= 4), 4 rows per instruction.
+// rows of K (w < 4) or V (w >= 4), 4 rows per instruction.  The loads are written as
+// inline asm so the compiler does not track them; every consumer waits for them
+// explicitly (vmcnt) before the barrier that publishes the stage.
 __device__ inline void dma_tile(const uint16_t *kbase, const uint16_t *vbase, int kb, int klast,
-                                char *stage, int wave, int lane)
+                                const char *stage, int wave, int lane)
 {
     const bool isv = wave >= 4;
     const uint16_t *g = isv ? vbase : kbase;
-    char *tdst = stage + (isv ? TILE_B : 0);
+    const uint32_t tdst = lds_offset(stage) + (isv ? TILE_B : 0);
     const int r0 = 16 * (wave & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -100,7 +116,11 @@ __device__ inline void dma_tile(const uint16_t *kbase, const uint16_t *vbase, in
         const int gchunk = (lane & 15) ^ (isv ? vswz(row) : kswz(row));
         const int key = min(kb + row, klast);
         const uint16_t *src = g + (int64_t)key * kHeadDim + gchunk * 8;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tdst + (r0 + 4 * i) * ROWB), 16, 0, 0);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(tdst + (uint32_t)((r0 + 4 * i) * ROWB));
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(dst), "v"(src)
+                     : "memory", "m0");
     }
 }
 
@@ -110,10 +130,12 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     // one stage never alias reads of the other (no spurious waits on the in-flight tile)
     __shared__ __align__(16) char lds_st0[STAGE_B];
     __shared__ __align__(16) char lds_st1[STAGE_B];
+    __shared__ __align__(16) char lds_st2[STAGE_B];
+    __shared__ __align__(16) char lds_st3[STAGE_B];
     __shared__ double wrev[kMaxPairs];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c = lane & 31;  // query within the wave's block (S^T column)
     const int hh = lane >> 5; // lane half
@@ -162,8 +184,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     const uint16_t *kbase = p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim;
     const uint16_t *vbase = p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim;
 
-    // ---- first tile and this lane's q row in flight; rotation table to LDS
-    dma_tile(kbase, vbase, 0, kend - 1, lds_st0, wave, lane);
+    // ---- loads in flight, oldest first: rotation table, this lane's q row, tiles 0 and 1
+    const double wr = tab.wrev[tid & (kMaxPairs - 1)];
     // rows past t read row t-1 (branch-free loads; their outputs are never written)
     const int iq = min(i, p.t - 1);
     const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
@@ -172,11 +194,15 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
     for (int s = 0; s < 8; ++s)
         qin[s] = ld16(qrow + 16 * s + 8 * hh);
+    dma_tile(kbase, vbase, 0, kend - 1, lds_st0, wave, lane);
+    if (ntiles > 1)
+        dma_tile(kbase, vbase, KT, kend - 1, lds_st1, wave, lane);
     if (tid < kMaxPairs)
-        wrev[tid] = tab.wrev[tid];
-    __syncthreads();
+        wrev[tid] = wr;
+    wg_barrier();
 
-    // ---- q prologue: rotate (fp32 trig with fp64 range reduction), round to f16
+    // ---- q prologue: rotate (fp32 trig with fp64 range reduction), scale, round to f16
+    const float sl2 = p.scale_log2;
     half8 qop[8];
     {
         const double posd = (double)qpos;
@@ -203,7 +229,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                     x0 = y0;
                     x1 = y1;
                 }
-                hv[m] = pack2h(x0, x1);
+                // the softmax scale (log2 units) rides on q: S^T comes out pre-scaled
+                hv[m] = pack2h(x0 * sl2, x1 * sl2);
             }
             qop[s] = __builtin_bit_cast(half8, hv);
         }
@@ -225,38 +252,114 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         }
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // tile 0 must have landed (tile 1 may still be in flight)
+    if (ntiles > 1)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wg_barrier();
 
     floatx16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
         o[db] = floatx16{0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = p.scale_log2;
+    // running max (log2 units) and the sum of the f16 probabilities, per query lane
+    float m_run = 0.f, l_run = 0.f;
+    bool first = true;
+    floatx16 sacc[2];  // S^T of the current tile, as (score - running max)
+    u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
 
-    auto step = [&](auto stg_c, int tile) {
+    // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of
+    // phases, the second group one phase behind.  A wave's phases alternate
+    //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
+    //   S(j): softmax of tile j                     (VALU)
+    // so on every SIMD one wave keeps the matrix core busy while the other does its
+    // softmax.  Each phase ends with a workgroup barrier.  Tile j sits in LDS stage
+    // j % 4 from two tiles before its first use (S^T in M(j)) until its last (PV in
+    // M(j+1) of the trailing group).
+    const int grp = wave >> 2;
+    const bool row_active = wave_valid;
+
+    auto tile_active = [&](int j) { return row_active && j * KT < kend_w; };
+
+    auto phase_m = [&](auto stg_c, int j) {
         constexpr int STG = decltype(stg_c)::value;
-        const char *st = STG ? lds_st1 : lds_st0;
-        const int kb = tile * KT;
-        if (tile + 1 < ntiles)
-            dma_tile(kbase, vbase, kb + KT, kend - 1, STG ? lds_st0 : lds_st1, wave, lane);
+        const char *st = STG == 0 ? lds_st0 : (STG == 1 ? lds_st1 : (STG == 2 ? lds_st2 : lds_st3));
+        const char *stp = STG == 0 ? lds_st3 : (STG == 1 ? lds_st0 : (STG == 2 ? lds_st1 : lds_st2));
+        char *st2 = STG == 0 ? lds_st2 : (STG == 1 ? lds_st3 : (STG == 2 ? lds_st0 : lds_st1));
+        const bool prefetch = j + 2 < ntiles;
+        if (prefetch)
+            dma_tile(kbase, vbase, (j + 2) * KT, kend - 1, st2, wave, lane);
+        // the matrix-core phase outranks the other group's softmax for issue slots
+        __builtin_amdgcn_s_setprio(1);
 
-        if (wave_valid && kb < kend_w) {
-            // S^T = K . Q^T for the tile's two 32-key blocks
-            floatx16 sacc[2];
+        // O^T += V^T . P^T for tile j-1 (stage of tile j-1); V^T by transposing reads
+        if (j >= 1 && tile_active(j - 1)) {
+            short4v vlo[2][4], vhi[2][4];
+            auto vread = [&](int x, int buf) {
+                const int rowoff = (32 * (x >> 1) + 16 * (x & 1)) * ROWB;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                half8 kop[8];
+                for (int db = 0; db < 4; ++db) {
+                    vlo[buf][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_short4_t *)(stp + vaddr[db] + rowoff));
+                    vhi[buf][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_short4_t *)(stp + vaddr[db] + rowoff + 8 * ROWB));
+                }
+            };
+            vread(0, 0);
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    kop[s] = *reinterpret_cast<const half8 *>(st + kaddr[s] + sb * 32 * ROWB);
-                sacc[sb] = floatx16{0.f};
+            for (int x = 0; x < 4; ++x) {
+                if (x + 1 < 4)
+                    vread(x + 1, (x + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                const half8 pop = __builtin_bit_cast(half8, pw[x]);
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[s], qop[s], sacc[sb], 0, 0, 0);
+                for (int db = 0; db < 4; ++db) {
+                    const short4v lo = vlo[x & 1][db], hi = vhi[x & 1][db];
+                    const half8 a = __builtin_bit_cast(
+                        half8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                          hi[0], hi[1], hi[2], hi[3]});
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pop, o[db], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
 
+        // S^T = K . Q^T for tile j: 16 MFMAs, K operands read four ahead; the
+        // accumulators start at -m_run so S^T leaves the MFMAs as (score - max)
+        if (j < ntiles && tile_active(j)) {
+            // the two key blocks' accumulation chains alternate, so consecutive MFMAs
+            // never wait on each other's results
+            half8 kq[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                kq[x] = *reinterpret_cast<const half8 *>(st + kaddr[x >> 1] + (x & 1) * 32 * ROWB);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const int sb = x & 1, s = x >> 1;
+                sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    kq[x & 3], qop[s], s == 0 ? floatx16(-m_run) : sacc[sb], 0, 0, 0);
+                if (x + 4 < 16)
+                    kq[x & 3] = *reinterpret_cast<const half8 *>(st + kaddr[(x + 4) >> 1] + ((x + 4) & 1) * 32 * ROWB);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // the trailing group's share of tile j+1 must land before the phase that
+        // starts the leading group's M(j+1)
+        if (grp == 1) {
+            if (prefetch)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        wg_barrier();
+    };
+
+    auto phase_s = [&](int j) {
+        if (tile_active(j)) {
+            const int kb = j * KT;
             // causal mask (only on tiles reaching past the block's first query)
             if (kb + KT - 1 > hist + i0) {
                 const int lim = qlimit - kb - 4 * hh;
@@ -276,67 +379,77 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 for (int r = 0; r < 16; ++r)
                     mx = fmaxf(mx, sacc[sb][r]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-            if (__any(mx > m_run + RESCALE_LOG2)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
+            mx = fmaxf(mx, __shfl_xor(mx, 32)); // max over the tile of (score - m_run)
+            // The first tile sets the max exactly; later tiles move it (and rescale the
+            // accumulators) only when some lane's max grows by more than 2^8.
+            if (first || __any(mx > RESCALE_LOG2)) {
+                const float d = first ? mx : fmaxf(mx, 0.f);
+                const float alpha = __builtin_amdgcn_exp2f(-d);
+                if (!first) {
+                    l_run *= alpha;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    o[db] *= alpha;
-                m_run = m_new;
+                    for (int db = 0; db < 4; ++db)
+                        o[db] *= alpha;
+                }
+                m_run += d;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        sacc[sb][r] -= d;
+                }
+                first = false;
             }
-            float rs = 0.f;
+            // probabilities, packed to f16 pairs (the PV operand) and summed as used
+            float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+            for (int x = 0; x < 4; ++x) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][r], sl2, -m_run));
-                    sacc[sb][r] = pv;
-                    rs += pv;
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * (x & 1) + 2 * jj;
+                    const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
+                                        __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
+                    const half2v ph = __builtin_convertvector(pf, half2v);
+                    pw[x][jj] = __builtin_bit_cast(uint32_t, ph);
+                    if (jj & 1)
+                        ls1 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls1, false);
+                    else
+                        ls0 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls0, false);
                 }
             }
-            l_run += rs;
+            l_run += ls0 + ls1;
+        }
+        // the leading group's share of tile j+1 must land before its M(j+1)
+        if (grp == 0) {
+            if (j + 2 < ntiles)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        wg_barrier();
+    };
 
-            // O^T += V^T . P^T ; V^T operands by transposing LDS reads
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int rowoff = (32 * sb + 16 * s2) * ROWB;
-                    short4v vlo[4], vhi[4];
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_short4_t *)(st + vaddr[db] + rowoff));
-                        vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_short4_t *)(st + vaddr[db] + rowoff + 8 * ROWB));
-                    }
-                    u32x4 pw;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        pw[j] = pack2h(sacc[sb][8 * s2 + 2 * j], sacc[sb][8 * s2 + 2 * j + 1]);
-                    const half8 pop = __builtin_bit_cast(half8, pw);
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        const short4v lo = vlo[db], hi = vhi[db];
-                        const half8 a = __builtin_bit_cast(
-                            half8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                              hi[0], hi[1], hi[2], hi[3]});
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pop, o[db], 0, 0, 0);
-                    }
+    if (grp == 1)
+        wg_barrier(); // the trailing group starts one phase late
+    for (int j0 = 0; j0 <= ntiles; j0 += 4) {
+        phase_m(std::integral_constant<int, 0>{}, j0);
+        if (j0 < ntiles) {
+            phase_s(j0);
+            phase_m(std::integral_constant<int, 1>{}, j0 + 1);
+            if (j0 + 1 < ntiles) {
+                phase_s(j0 + 1);
+                phase_m(std::integral_constant<int, 2>{}, j0 + 2);
+                if (j0 + 2 < ntiles) {
+                    phase_s(j0 + 2);
+                    phase_m(std::integral_constant<int, 3>{}, j0 + 3);
+                    if (j0 + 3 < ntiles)
+                        phase_s(j0 + 3);
                 }
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-
-    for (int tile = 0; tile < ntiles; tile += 2) {
-        step(std::integral_constant<int, 0>{}, tile);
-        if (tile + 1 < ntiles)
-            step(std::integral_constant<int, 1>{}, tile + 1);
     }
+    if (grp == 0)
+        wg_barrier(); // same barrier count for both groups
 
     // ---- normalise and write: lane holds dims 32db + 8*(r/4) + 4*hh + r%4 of query c
     const float l_tot = l_run + __shfl_xor(l_run, 32);
