@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this attention path runs on a single MI355X "
@@ -176,6 +178,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     kv.lib()
+
+    if args.copy_calibration:
+        # a plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for 1 GiB each way
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     log(f"[bench] prefill {args.workload}: warmup {args.warmup}, steps {args.steps}")
     cfg, ms_step, k_ms, flops = bench_prefill(kv, W, args.workload, args.steps, args.warmup)

@@ -27,23 +27,23 @@
 // enough in f16) and most tiles skip the 64 multiplies.  The causal mask is applied only
 // on tiles that reach past the first query of the block.
 //
-// LDS (four stages).  K and V tiles go from HBM/L2 straight
-// into LDS (global_load_lds_dwordx4: lane L of a wave's load lands at byte 16 L of a
-// 1 KB LDS block), so staging costs no registers and no VALU; each tile's loads are
-// issued two tiles ahead of its first use.  (In each 16-lane group of that load, lanes
-// 16r .. 16r+15 fill row r of the 4-row block: the swizzle picks which global chunk each
-// lane fetches.)  Both tiles are row-major [64 keys][256 B] with
-// the 16-byte chunk index xor-swizzled by the row:
-//   K: chunk ^ (key & 15)        -- the S^T A-operand reads (16 B of 32 consecutive keys)
-//                                   hit distinct banks;
-//   V: chunk ^ ((key & 3) << 2)  -- the PV A-operand comes from ds_read_b64_tr_b16: in
-//                                   each 16-lane group, lane 4k+m points at 4 dims of
-//                                   key row k and lane i receives dim i of the 4 rows,
-//                                   i.e. 4 consecutive keys of one head dim (V^T).
-// All per-lane LDS addresses are computed once; the phase loop is unrolled over the four
-// stages so they are immediate offsets (and separate objects, so loads into one stage
-// never make the compiler wait before reading another), and the operand reads are
-// software-pipelined ahead of the MFMAs that consume them.
+// LDS (four stages, 32 KB each).
+//   K tile: row-major [64 keys][256 B] with the 16-byte chunk index xor-swizzled by the
+//           row (chunk ^ (key & 15)), so the S^T A-operand reads (16 B of 32 consecutive
+//           keys) hit distinct banks.  It goes from HBM/L2 straight into LDS
+//           (global_load_lds_dwordx4: lane L of a wave's load lands at byte 16 L of a
+//           1 KB block; the swizzle picks which global chunk each lane fetches).
+//   V tile: pre-transposed for the PV A-operand, [4 groups of 16 keys][2 lane halves]
+//           [128 dims][8 keys]: the 8 keys of (group, half) are the ones that half's
+//           lanes contribute to one 16-key MFMA step, so each A operand is a single
+//           16-byte read; the dim index is xor-swizzled inside groups of 8 to spread the
+//           transposing writes.  V rows are staged through registers (2 rows x 16 B per
+//           thread) one phase pair before they are written.
+// A tile's K is issued two tiles ahead of its first use and its V one tile ahead.  All
+// per-lane LDS addresses are computed once; the phase loop is unrolled over the four
+// stages so they are immediate offsets (and separate objects, so the compiler never
+// waits on one stage before reading another), and the operand reads run four ahead of
+// the MFMAs that consume them.
 // Grid order: heavier (later) work first; when the number of (unit, KV head) pairs is a
 // multiple of 8, all workgroups of one pair go to the same XCD (workgroups are dealt to
 // the 8 XCDs round-robin) so its K/V stays in that XCD's L2.
@@ -67,8 +67,6 @@ constexpr int TILE_B = KT * ROWB;      // 16 KB per tensor per stage
 constexpr int STAGE_B = 2 * TILE_B;    // K tile, then V tile
 constexpr float RESCALE_LOG2 = 8.f;    // lazy-rescale threshold (log2 units)
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4_t;
 
 struct PrefillParams {
     const uint16_t *q;
@@ -92,35 +90,68 @@ struct PrefillParams {
 __device__ inline void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ inline int kswz(int key) { return key & 15; }
-__device__ inline int vswz(int key) { return (key & 3) << 2; }
 
 __device__ inline uint32_t lds_offset(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
-// Issue one tile (keys kb .. kb+63, clamped to klast) into an LDS stage: wave w moves 16
-// rows of K (w < 4) or V (w >= 4), 4 rows per instruction.  The loads are written as
-// inline asm so the compiler does not track them; every consumer waits for them
-// explicitly (vmcnt) before the barrier that publishes the stage.
-__device__ inline void dma_tile(const uint16_t *kbase, const uint16_t *vbase, int kb, int klast,
-                                const char *stage, int wave, int lane)
+// Issue the K rows of one tile (keys kb .. kb+63, clamped to klast) into an LDS stage:
+// wave w moves rows 8w .. 8w+7, 4 rows per instruction.  The loads are inline asm so
+// the compiler does not track them; they are waited for explicitly (vmcnt) before the
+// barrier that publishes the stage.
+__device__ inline void dma_k(const uint16_t *kbase, int kb, int klast, const char *stage, int wave,
+                             int lane)
 {
-    const bool isv = wave >= 4;
-    const uint16_t *g = isv ? vbase : kbase;
-    const uint32_t tdst = lds_offset(stage) + (isv ? TILE_B : 0);
-    const int r0 = 16 * (wave & 3);
+    const uint32_t tdst = lds_offset(stage);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = r0 + 4 * i + (lane >> 4);
-        const int gchunk = (lane & 15) ^ (isv ? vswz(row) : kswz(row));
+    for (int i = 0; i < 2; ++i) {
+        const int r0 = 8 * wave + 4 * i;
+        const int row = r0 + (lane >> 4);
+        const int gchunk = (lane & 15) ^ kswz(row);
         const int key = min(kb + row, klast);
-        const uint16_t *src = g + (int64_t)key * kHeadDim + gchunk * 8;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(tdst + (uint32_t)((r0 + 4 * i) * ROWB));
+        const uint16_t *src = kbase + (int64_t)key * kHeadDim + gchunk * 8;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(tdst + (uint32_t)(r0 * ROWB));
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                      :
                      : "s"(dst), "v"(src)
                      : "memory", "m0");
+    }
+}
+
+// V staging: thread tid owns lane half hh = (tid >> 6) & 1 of key group grp = tid >> 7,
+// the 8-dim chunk m = (tid >> 2) & 15 and the key pair kq = tid & 3 of that half's list
+// (keys 16 grp + 4 hh + {0, 1, 2, 3, 8, 9, 10, 11}).
+struct VRegs {
+    u32x4 a, b;
+};
+
+__device__ inline int vkey(int tid, int which)
+{
+    const int kq = tid & 3, hh = (tid >> 6) & 1, grp = tid >> 7;
+    const int pos = 2 * kq + which;
+    return 16 * grp + 4 * hh + (pos < 4 ? pos : pos + 4);
+}
+
+__device__ inline void load_v(VRegs &r, const uint16_t *vbase, int kb, int klast, int tid)
+{
+    const int m = (tid >> 2) & 15;
+    r.a = ld16(vbase + (int64_t)min(kb + vkey(tid, 0), klast) * kHeadDim + 8 * m);
+    r.b = ld16(vbase + (int64_t)min(kb + vkey(tid, 1), klast) * kHeadDim + 8 * m);
+}
+
+__device__ inline int vpos(int dim) { return dim ^ ((dim >> 3) & 7); }
+
+__device__ inline void store_v(const VRegs &r, char *stage, int tid)
+{
+    const int kq = tid & 3, m = (tid >> 2) & 15, hh = (tid >> 6) & 1, grp = tid >> 7;
+    char *vt = stage + TILE_B + (grp * 2 + hh) * kHeadDim * 16 + 4 * kq;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t x = r.a[e >> 1], y = r.b[e >> 1];
+        const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(y, x, 0x07060302u)
+                                   : __builtin_amdgcn_perm(y, x, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vt + vpos(8 * m + e) * 16) = w;
     }
 }
 
@@ -194,9 +225,11 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
     for (int s = 0; s < 8; ++s)
         qin[s] = ld16(qrow + 16 * s + 8 * hh);
-    dma_tile(kbase, vbase, 0, kend - 1, lds_st0, wave, lane);
+    dma_k(kbase, 0, kend - 1, lds_st0, wave, lane);
     if (ntiles > 1)
-        dma_tile(kbase, vbase, KT, kend - 1, lds_st1, wave, lane);
+        dma_k(kbase, KT, kend - 1, lds_st1, wave, lane);
+    VRegs vr;
+    load_v(vr, vbase, 0, kend - 1, tid);
     if (tid < kMaxPairs)
         wrev[tid] = wr;
     wg_barrier();
@@ -242,21 +275,15 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     for (int s = 0; s < 8; ++s)
         kaddr[s] = c * ROWB + (((2 * s + hh) ^ kswz(c)) << 4);
     int vaddr[4];
-    {
-        const int grp = lane >> 4, j = lane & 15, kk = j >> 2, m = j & 3;
-        const int row = 4 * (grp >> 1) + kk;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int chunk = 4 * db + 2 * (grp & 1) + (m >> 1);
-            vaddr[db] = TILE_B + row * ROWB + ((chunk ^ vswz(row)) << 4) + 8 * (m & 1);
-        }
-    }
+    for (int db = 0; db < 4; ++db)
+        vaddr[db] = TILE_B + (hh * kHeadDim + vpos(32 * db + c)) * 16;
 
-    // tile 0 must have landed (tile 1 may still be in flight)
+    // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    store_v(vr, lds_st0, tid);
     if (ntiles > 1)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        load_v(vr, vbase, KT, kend - 1, tid);
     wg_barrier();
 
     floatx16 o[4];
@@ -287,40 +314,38 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const char *st = STG == 0 ? lds_st0 : (STG == 1 ? lds_st1 : (STG == 2 ? lds_st2 : lds_st3));
         const char *stp = STG == 0 ? lds_st3 : (STG == 1 ? lds_st0 : (STG == 2 ? lds_st1 : lds_st2));
         char *st2 = STG == 0 ? lds_st2 : (STG == 1 ? lds_st3 : (STG == 2 ? lds_st0 : lds_st1));
-        const bool prefetch = j + 2 < ntiles;
-        if (prefetch)
-            dma_tile(kbase, vbase, (j + 2) * KT, kend - 1, st2, wave, lane);
+        char *st1 = STG == 0 ? lds_st1 : (STG == 1 ? lds_st2 : (STG == 2 ? lds_st3 : lds_st0));
+        // tile j+1: its V rows (loaded one phase pair ago) into its stage; all of this
+        // wave's loads are complete afterwards, including its K share of tile j+1
+        if (j + 1 < ntiles) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            store_v(vr, st1, tid);
+        }
+        // tile j+2: K straight into its stage, V rows into registers
+        // (V first: the compiler's own wait before reusing vr must not cover the K loads)
+        if (j + 2 < ntiles) {
+            load_v(vr, vbase, (j + 2) * KT, kend - 1, tid);
+            dma_k(kbase, (j + 2) * KT, kend - 1, st2, wave, lane);
+        }
         // the matrix-core phase outranks the other group's softmax for issue slots
         __builtin_amdgcn_s_setprio(1);
 
-        // O^T += V^T . P^T for tile j-1 (stage of tile j-1); V^T by transposing reads
+        // O^T += V^T . P^T for tile j-1: 16 MFMAs (key step g = 2 sb + s2, dim block db),
+        // V^T operands read four ahead
         if (j >= 1 && tile_active(j - 1)) {
-            short4v vlo[2][4], vhi[2][4];
-            auto vread = [&](int x, int buf) {
-                const int rowoff = (32 * (x >> 1) + 16 * (x & 1)) * ROWB;
+            half8 vq[4];
 #pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    vlo[buf][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_short4_t *)(stp + vaddr[db] + rowoff));
-                    vhi[buf][db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_short4_t *)(stp + vaddr[db] + rowoff + 8 * ROWB));
-                }
-            };
-            vread(0, 0);
+            for (int x = 0; x < 4; ++x)
+                vq[x] = *reinterpret_cast<const half8 *>(stp + vaddr[x & 3] + (x >> 2) * 2 * kHeadDim * 16);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                if (x + 1 < 4)
-                    vread(x + 1, (x + 1) & 1);
-                __builtin_amdgcn_sched_barrier(0);
-                const half8 pop = __builtin_bit_cast(half8, pw[x]);
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const short4v lo = vlo[x & 1][db], hi = vhi[x & 1][db];
-                    const half8 a = __builtin_bit_cast(
-                        half8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                          hi[0], hi[1], hi[2], hi[3]});
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pop, o[db], 0, 0, 0);
-                }
+            for (int x = 0; x < 16; ++x) {
+                const int gi = x >> 2, db = x & 3;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[x & 3], __builtin_bit_cast(half8, pw[gi]),
+                                                               o[db], 0, 0, 0);
+                if (x + 4 < 16)
+                    vq[x & 3] = *reinterpret_cast<const half8 *>(stp + vaddr[(x + 4) & 3] +
+                                                                  ((x + 4) >> 2) * 2 * kHeadDim * 16);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -346,14 +371,6 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        // the trailing group's share of tile j+1 must land before the phase that
-        // starts the leading group's M(j+1)
-        if (grp == 1) {
-            if (prefetch)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
         wg_barrier();
     };
 
@@ -418,13 +435,6 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 }
             }
             l_run += ls0 + ls1;
-        }
-        // the leading group's share of tile j+1 must land before its M(j+1)
-        if (grp == 0) {
-            if (j + 2 < ntiles)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         wg_barrier();
     };
