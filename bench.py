@@ -34,6 +34,27 @@ METRIC = "prefill attn TFLOP/s (% MFMA peak) + decode KV-cache GB/s (% HBM peak)
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense f16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes of this script,
+# scaled by what the same counters read for a plain 1 GiB device copy (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0; profiles/hbm_traffic_counters.md).  `src` is the sha256 of the kernel
+# source and the shared device header at measurement time: once either changes, the
+# figure no longer describes the kernel and `traffic` is reported as null.
+TRAFFIC = {
+    "prefill_attn:qwen1p5b_prefill_t1024": {
+        "bytes": 269.142e6,
+        "src": ("329ffff231d871dde6badcf07219febf84acc7bbdb483bbfe1edad977d00ca5b",
+                "090b0feb4425e0e50f391526c9cf2d400cce8f7fc1080f177b2d1db555b5f0df")},
+    "decode_split:qwen1p5b_decode_l4096_b32": {
+        "bytes": 2.82754e9,
+        "src": ("598c87dd6c477fb2222df469535a04f0f3f817248b59182b139fe17e6a52a8dd",
+                "090b0feb4425e0e50f391526c9cf2d400cce8f7fc1080f177b2d1db555b5f0df")},
+    "decode_split:yarn_decode_l32k_b64": {
+        "bytes": 23.0181e9,
+        "src": ("598c87dd6c477fb2222df469535a04f0f3f817248b59182b139fe17e6a52a8dd",
+                "090b0feb4425e0e50f391526c9cf2d400cce8f7fc1080f177b2d1db555b5f0df")},
+}
+KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_split": "decode.hip"}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -51,6 +72,19 @@ def decode_bytes(lens, hq, hkv, d):
     lens = [int(x) for x in lens]
     per_unit_fixed = 2 * hkv * d * 2 + 2 * hkv * d * 2 + 2 * hq * d * 2
     return sum(2 * hkv * d * 2 * L for L in lens) + per_unit_fixed * len(lens)
+
+
+def traffic(kernel, workload):
+    """Counter-measured HBM bytes per launch, or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    rec = TRAFFIC.get(f"{kernel}:{workload}")
+    if rec is None:
+        return None
+    csrc = os.path.join(ROOT, "kv_cache_causal_rope_amd", "csrc")
+    now = tuple(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+                for f in (KERNEL_SOURCES[kernel], "device_common.h"))
+    return rec["bytes"] if now == rec["src"] else None
 
 
 def make_events(n):
@@ -160,7 +194,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen1p5b_prefill_t1024")
-    ap.add_argument("--cpu-units", type=int, default=2)
+    ap.add_argument("--cpu-units", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -212,7 +246,8 @@ def main():
                            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                            "roofline": {"bound": "hbm", "achieved": round(kgbs, 1),
                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                        "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": None}})
+                                        "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                                        "traffic": traffic("decode_split", name)}})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -238,7 +273,7 @@ def main():
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic("prefill_attn", cfg.name)},
         "decode": decode,
         "cpu_baseline": cpu,
     }
