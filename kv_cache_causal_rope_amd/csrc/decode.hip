@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, RopeT
             sacc[r] = sv;
             mx = fmaxf(mx, sv);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = half_max(mx);
         const float m_new = fmaxf(m_run, mx); // finite: key kb < k1 is always valid
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         float rs = 0.f;
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, RopeT
     }
 
     // ---- merge the four waves' states (a wave without keys has m = -inf, l = 0, o = 0)
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = half_sum(l_run);
     if (c < GS && hh == 0) {
         sm.wm[wave][c] = m_run;
         sm.wl[wave][c] = l_tot;

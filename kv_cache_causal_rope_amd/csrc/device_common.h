@@ -100,4 +100,24 @@ __device__ inline uint32_t pack2h(float a, float b)
 
 __device__ inline uint16_t qnan16() { return 0x7e00u; }
 
+// Combine a lane's value with the one 32 lanes away (lanes l and l ^ 32) without LDS:
+// v_permlane32_swap exchanges lanes 32-63 of one register with lanes 0-31 of another, so
+// after swapping two copies of x every lane holds {x[l], x[l ^ 32]} in some order.
+__device__ inline floatx2 swap_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return floatx2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+__device__ inline float half_max(float x)
+{
+    const floatx2 r = swap_halves(x);
+    return __builtin_fmaxf(r[0], r[1]);
+}
+__device__ inline float half_sum(float x)
+{
+    const floatx2 r = swap_halves(x);
+    return r[0] + r[1];
+}
+
 } // namespace kvrope

@@ -11,26 +11,37 @@
 //
 // Work decomposition.  For one (unit, KV head) the work items are (block of 32 new
 // tokens, query head of the group), numbered token-block-major.  A workgroup of 8 waves
-// takes 8 consecutive items (one per wave), so it spans at most two adjacent token
-// blocks and shares every K/V tile it stages in LDS among 8 x 32 query rows; 8 waves
-// also keep the 4 SIMDs of a CU evenly loaded for any group size.  Per 64-key tile a
+// takes 8 consecutive items (one per wave), so it spans few adjacent token blocks and
+// shares every K/V tile it stages in LDS among 8 x 32 query rows.  Per 64-key tile a
 // wave issues 32 MFMAs (v_mfma_f32_32x32x16_f16):
 //   S^T (64 keys x 32 queries) = K . Q^T        -- 2 key blocks x 8 head-dim steps
 //   O^T (128 dims x 32 queries) += V^T . P^T    -- 2 key blocks x 2 key steps x 4 dim blocks
 // Working on S^T puts one query in each lane (lane l: query l % 32, half l / 32), so the
-// row max is a per-lane reduction plus one cross-half exchange, and the probabilities
-// are already in the B-operand layout of the PV product (the key order inside each
-// 16-key step is permuted consistently on both operands, which the reduction allows).
-// Softmax runs in fp32 in the log2 domain (exp2 of scale*log2(e)-scaled scores) with the
-// running max / running sum rescaling, applied lazily: the accumulators are rescaled only
-// when some lane's max grows by more than 2^8, so the probabilities stay <= 256 (exact
-// enough in f16) and most tiles skip the 64 multiplies.  The causal mask is applied only
-// on tiles that reach past the first query of the block.
+// probabilities come out of the softmax already in the B-operand layout of the PV
+// product (the key order inside each 16-key step is permuted consistently on both
+// operands, which the reduction allows).
 //
-// LDS (four stages, 32 KB each).
-//   K tile: row-major [64 keys][256 B] with the 16-byte chunk index xor-swizzled by the
-//           row (chunk ^ (key & 15)), so the S^T A-operand reads (16 B of 32 consecutive
-//           keys) hit distinct banks.  It goes from HBM/L2 straight into LDS
+// Softmax: fp32, log2 domain (q carries scale * log2(e)).  The score accumulators start
+// at -m (m = the row's reference max), so S^T leaves the matrix core as (score - m).  m
+// is set exactly from a row's first tile and is otherwise left alone: the probabilities
+// 2^(score - m) are rounded to f16 for the PV product, so they may grow up to the f16
+// range (relative precision is the same at any magnitude) before anything must move.
+// A tile whose probabilities overflow f16 -- seen as an infinite row sum -- takes the
+// exact path: m moves to the tile's max, O and the running sum are rescaled and the
+// tile's probabilities are recomputed.  So the common tile costs no max reduction.
+//
+// Two wave groups in ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run the same
+// phase sequence, the second one phase behind, so while one wave of a SIMD runs its 32
+// MFMAs the other runs its softmax on the vector ALU.  Every phase ends in a workgroup
+// barrier.  Per MFMA phase the operand reads (16 bytes per lane, one per MFMA) run eight
+// ahead of the MFMAs across the PV -> QK boundary.
+//
+// LDS: a four-stage ring of (K tile, V tile), 16 KB each.  The K regions of all stages
+// sit in the first 64 KB and the V regions in the second, so every operand read uses an
+// immediate offset from one per-lane base.
+//   K tile: row-major [64 keys][256 B], 16-byte chunk index xor-swizzled by the row
+//           (chunk ^ (key & 15)) so the S^T A-operand reads (16 B of 32 consecutive keys)
+//           hit distinct banks.  It goes from HBM/L2 straight into LDS
 //           (global_load_lds_dwordx4: lane L of a wave's load lands at byte 16 L of a
 //           1 KB block; the swizzle picks which global chunk each lane fetches).
 //   V tile: pre-transposed for the PV A-operand, [4 groups of 16 keys][2 lane halves]
@@ -39,11 +50,8 @@
 //           16-byte read; the dim index is xor-swizzled inside groups of 8 to spread the
 //           transposing writes.  V rows are staged through registers (2 rows x 16 B per
 //           thread) one phase pair before they are written.
-// A tile's K is issued two tiles ahead of its first use and its V one tile ahead.  All
-// per-lane LDS addresses are computed once; the phase loop is unrolled over the four
-// stages so they are immediate offsets (and separate objects, so the compiler never
-// waits on one stage before reading another), and the operand reads run four ahead of
-// the MFMAs that consume them.
+// Tile loads use a wave-uniform tile base address plus per-lane 32-bit offsets fixed for
+// the whole kernel; only a workgroup's last, partial tile clamps rows to the last key.
 // Grid order: heavier (later) work first; when the number of (unit, KV head) pairs is a
 // multiple of 8, all workgroups of one pair go to the same XCD (workgroups are dealt to
 // the 8 XCDs round-robin) so its K/V stays in that XCD's L2.
@@ -64,9 +72,9 @@ constexpr int NW = 8;                  // waves per workgroup
 constexpr int NT = NW * 64;            // threads per workgroup
 constexpr int ROWB = kHeadDim * 2;     // bytes per K / V row
 constexpr int TILE_B = KT * ROWB;      // 16 KB per tensor per stage
-constexpr int STAGE_B = 2 * TILE_B;    // K tile, then V tile
-constexpr float RESCALE_LOG2 = 8.f;    // lazy-rescale threshold (log2 units)
-
+constexpr int NSTAGE = 4;
+constexpr int VREG_B = NSTAGE * TILE_B; // V regions start after the four K regions
+constexpr int RD = 6;                  // operand reads in flight ahead of the MFMAs
 
 struct PrefillParams {
     const uint16_t *q;
@@ -96,25 +104,26 @@ __device__ inline uint32_t lds_offset(const void *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
-// Issue the K rows of one tile (keys kb .. kb+63, clamped to klast) into an LDS stage:
-// wave w moves rows 8w .. 8w+7, 4 rows per instruction.  The loads are inline asm so
-// the compiler does not track them; they are waited for explicitly (vmcnt) before the
-// barrier that publishes the stage.
-__device__ inline void dma_k(const uint16_t *kbase, int kb, int klast, const char *stage, int wave,
-                             int lane)
+// Per-lane byte offsets of the K rows a lane moves into LDS: wave w moves rows
+// 8w .. 8w+7, 4 rows per instruction, lane L taking row 4i + L/16 of its group and the
+// global chunk that lands in LDS chunk L % 16 of that row.
+__device__ inline int krow(int wave, int lane, int i) { return 8 * wave + 4 * i + (lane >> 4); }
+__device__ inline uint32_t koffset(int row, int lane)
 {
-    const uint32_t tdst = lds_offset(stage);
+    return (uint32_t)(row * ROWB + (((lane & 15) ^ kswz(row)) << 4));
+}
+
+// K rows of one tile straight into an LDS stage.  `tile` is the wave-uniform address of
+// the tile's first row; the loads are inline asm so the compiler does not track them;
+// they are waited for explicitly (vmcnt) before the barrier that publishes the stage.
+__device__ inline void dma_k(const char *tile, const uint32_t (&off)[2], uint32_t stage_lds, int wave)
+{
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int r0 = 8 * wave + 4 * i;
-        const int row = r0 + (lane >> 4);
-        const int gchunk = (lane & 15) ^ kswz(row);
-        const int key = min(kb + row, klast);
-        const uint16_t *src = kbase + (int64_t)key * kHeadDim + gchunk * 8;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(tdst + (uint32_t)(r0 * ROWB));
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+        const uint32_t dst = stage_lds + (uint32_t)((8 * wave + 4 * i) * ROWB);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
-                     : "s"(dst), "v"(src)
+                     : "s"(dst), "v"(off[i]), "s"(tile)
                      : "memory", "m0");
     }
 }
@@ -133,37 +142,55 @@ __device__ inline int vkey(int tid, int which)
     return 16 * grp + 4 * hh + (pos < 4 ? pos : pos + 4);
 }
 
-__device__ inline void load_v(VRegs &r, const uint16_t *vbase, int kb, int klast, int tid)
+__device__ inline uint32_t voffset(int key, int tid) { return (uint32_t)(key * ROWB + 16 * ((tid >> 2) & 15)); }
+
+__device__ inline void load_v(VRegs &r, const char *tile, const uint32_t (&off)[2])
 {
-    const int m = (tid >> 2) & 15;
-    r.a = ld16(vbase + (int64_t)min(kb + vkey(tid, 0), klast) * kHeadDim + 8 * m);
-    r.b = ld16(vbase + (int64_t)min(kb + vkey(tid, 1), klast) * kHeadDim + 8 * m);
+    r.a = *reinterpret_cast<const u32x4 *>(tile + off[0]);
+    r.b = *reinterpret_cast<const u32x4 *>(tile + off[1]);
 }
 
 __device__ inline int vpos(int dim) { return dim ^ ((dim >> 3) & 7); }
 
-__device__ inline void store_v(const VRegs &r, char *stage, int tid)
+// LDS byte offset (stage 0) where thread tid writes dim 8m + e of its two keys.
+__device__ inline uint32_t vstore_offset(int tid, int e)
 {
     const int kq = tid & 3, m = (tid >> 2) & 15, hh = (tid >> 6) & 1, grp = tid >> 7;
-    char *vt = stage + TILE_B + (grp * 2 + hh) * kHeadDim * 16 + 4 * kq;
+    return (uint32_t)(VREG_B + ((grp * 2 + hh) * kHeadDim + vpos(8 * m + e)) * 16 + 4 * kq);
+}
+
+// Transposing write of the staged rows into the V region of stage STG (an immediate
+// offset from the thread's eight stage-0 addresses): dim 8m + e of the first key goes to
+// the low half of its word, of the second key to the high half.  The 16-bit stores take
+// either half of a register directly, so the transpose costs no vector ALU work (as
+// plain C++ the compiler would merge each pair into one 32-bit store behind a v_perm).
+// They are inline asm: the barrier that publishes the stage waits for them (lgkmcnt),
+// and LDS operations complete in order, so later compiler-counted waits stay correct.
+template <int STG>
+__device__ inline void store_v(const VRegs &r, char *lds, const uint32_t (&vst)[8])
+{
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+        const uint32_t addr = lds_offset(lds) + vst[e];
         const uint32_t x = r.a[e >> 1], y = r.b[e >> 1];
-        const uint32_t w = (e & 1) ? __builtin_amdgcn_perm(y, x, 0x07060302u)
-                                   : __builtin_amdgcn_perm(y, x, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(vt + vpos(8 * m + e) * 16) = w;
+        if (e & 1)
+            asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2\n\tds_write_b16_d16_hi %0, %3 offset:%4"
+                         :
+                         : "v"(addr), "v"(x), "i"(STG * TILE_B), "v"(y), "i"(STG * TILE_B + 2)
+                         : "memory");
+        else
+            asm volatile("ds_write_b16 %0, %1 offset:%2\n\tds_write_b16 %0, %3 offset:%4"
+                         :
+                         : "v"(addr), "v"(x), "i"(STG * TILE_B), "v"(y), "i"(STG * TILE_B + 2)
+                         : "memory");
     }
 }
 
 __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab)
 {
-    // two pipeline stages as separate objects, so the compiler can tell that loads into
-    // one stage never alias reads of the other (no spurious waits on the in-flight tile)
-    __shared__ __align__(16) char lds_st0[STAGE_B];
-    __shared__ __align__(16) char lds_st1[STAGE_B];
-    __shared__ __align__(16) char lds_st2[STAGE_B];
-    __shared__ __align__(16) char lds_st3[STAGE_B];
-    __shared__ double wrev[kMaxPairs];
+    __shared__ __align__(16) char lds[2 * NSTAGE * TILE_B];
+    __shared__ double wdim[kMaxPairs]; // revolutions per position of dim pair dp (0: unrotated)
+    __shared__ float sdim[kMaxPairs];  // output scale of dim pair dp
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,15 +235,64 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     }
     const int tb_last = last_item / p.G;
     const int kend = hist + min((tb_last + 1) * QB, p.t); // keys the workgroup needs
+    const int klast = kend - 1;
     const int ntiles = (kend + KT - 1) / KT;
     const int kend_w = hist + min(i0 + QB, p.t);        // keys this wave needs
     const int qlimit = hist + i;                         // last visible key of the lane's query
 
-    const uint16_t *kbase = p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim;
-    const uint16_t *vbase = p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim;
+    const char *kbase = reinterpret_cast<const char *>(p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
+    const char *vbase = reinterpret_cast<const char *>(p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
+
+    // per-lane tile offsets (full tiles) and the LDS addresses of this thread
+    uint32_t koff[2], voff[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        koff[r] = koffset(krow(wave, lane, r), lane);
+        voff[r] = voffset(vkey(tid, r), tid);
+    }
+    const uint32_t lds_base = lds_offset(lds);
+    uint32_t vst[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        vst[e] = vstore_offset(tid, e);
+
+    // Tile loads.  Rows at or past kend clamp to the last key (finite values; they are
+    // masked or carry probability 0), and only the last tile can hold such rows.
+    auto issue_k = [&](int j, uint32_t stage_lds) {
+        const int kb = j * KT;
+        const char *tile = kbase + (int64_t)kb * ROWB;
+        if (kb + KT <= kend) {
+            dma_k(tile, koff, stage_lds, wave);
+        } else {
+            // the source row clamps; the swizzled chunk stays the destination row's
+            uint32_t o[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int row = krow(wave, lane, r);
+                o[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
+            }
+            dma_k(tile, o, stage_lds, wave);
+        }
+    };
+    auto issue_v = [&](VRegs &r, int j) {
+        const int kb = j * KT;
+        // (readfirstlane keeps the whole tile offset in the scalar base address)
+        const char *tile = vbase + (int64_t)__builtin_amdgcn_readfirstlane(kb) * ROWB;
+        if (kb + KT <= kend) {
+            load_v(r, tile, voff);
+        } else {
+            uint32_t o[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                o[x] = voffset(min(vkey(tid, x), klast - kb), tid);
+            load_v(r, tile, o);
+        }
+    };
 
     // ---- loads in flight, oldest first: rotation table, this lane's q row, tiles 0 and 1
-    const double wr = tab.wrev[tid & (kMaxPairs - 1)];
+    const int dp_t = tid & (kMaxPairs - 1);
+    const bool rot_t = 2 * dp_t >= tab.off;
+    const double wr = tab.wrev[rot_t ? dp_t - (tab.off >> 1) : 0];
     // rows past t read row t-1 (branch-free loads; their outputs are never written)
     const int iq = min(i, p.t - 1);
     const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
@@ -225,156 +301,206 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
     for (int s = 0; s < 8; ++s)
         qin[s] = ld16(qrow + 16 * s + 8 * hh);
-    dma_k(kbase, 0, kend - 1, lds_st0, wave, lane);
+    issue_k(0, lds_base);
     if (ntiles > 1)
-        dma_k(kbase, KT, kend - 1, lds_st1, wave, lane);
+        issue_k(1, lds_base + TILE_B);
     VRegs vr;
-    load_v(vr, vbase, 0, kend - 1, tid);
-    if (tid < kMaxPairs)
-        wrev[tid] = wr;
+    issue_v(vr, 0);
+    const float sl2 = p.scale_log2;
+    if (tid < kMaxPairs) {
+        wdim[tid] = rot_t ? wr : 0.0;
+        sdim[tid] = rot_t ? (float)tab.mscale * sl2 : sl2;
+    }
     wg_barrier();
 
-    // ---- q prologue: rotate (fp32 trig with fp64 range reduction), scale, round to f16
-    const float sl2 = p.scale_log2;
+    // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16
     half8 qop[8];
     {
         const double posd = (double)qpos;
-        const float msc = (float)tab.mscale;
-        const int off = tab.off;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
+            const int dp0 = 8 * s + 4 * hh;
             const u32x4 in = qin[s];
             u32x4 hv;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int dim = 16 * s + 8 * hh + 2 * m;
-                const uint32_t w = in[m];
-                float x0 = lo2f(w), x1 = hi2f(w);
-                if (dim >= off) {
-                    const int j = (dim - off) >> 1;
-                    double rev = posd * wrev[j];
-                    rev -= floor(rev);
-                    const float rf = (float)rev;
-                    const float cs = __builtin_amdgcn_cosf(rf) * msc;
-                    const float sn = __builtin_amdgcn_sinf(rf) * msc;
-                    const float y0 = x0 * cs - x1 * sn;
-                    const float y1 = x0 * sn + x1 * cs;
-                    x0 = y0;
-                    x1 = y1;
-                }
-                // the softmax scale (log2 units) rides on q: S^T comes out pre-scaled
-                hv[m] = pack2h(x0 * sl2, x1 * sl2);
+                const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp0 + m]);
+                const float sc = sdim[dp0 + m];
+                const float cs = __builtin_amdgcn_cosf(rf) * sc;
+                const float sn = __builtin_amdgcn_sinf(rf) * sc;
+                const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
+                const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
+                hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
             }
             qop[s] = __builtin_bit_cast(half8, hv);
         }
     }
 
-    // ---- per-lane LDS byte addresses inside a stage
+    // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
+    const char *kread = lds + c * ROWB;
     int kaddr[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        kaddr[s] = c * ROWB + (((2 * s + hh) ^ kswz(c)) << 4);
+        kaddr[s] = ((2 * s + hh) ^ kswz(c)) << 4;
+    const char *vread = lds + VREG_B + hh * kHeadDim * 16;
     int vaddr[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-        vaddr[db] = TILE_B + (hh * kHeadDim + vpos(32 * db + c)) * 16;
+        vaddr[db] = vpos(32 * db + c) * 16;
 
     // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    store_v(vr, lds_st0, tid);
+    store_v<0>(vr, lds, vst);
     if (ntiles > 1)
-        load_v(vr, vbase, KT, kend - 1, tid);
+        issue_v(vr, 1);
     wg_barrier();
 
     floatx16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
         o[db] = floatx16{0.f};
-    // running max (log2 units) and the sum of the f16 probabilities, per query lane
+    // reference max (log2 units) and the running sum of the f16 probabilities
     float m_run = 0.f, l_run = 0.f;
+    floatx16 mneg = floatx16{0.f}; // -m_run in every accumulator slot (S^T start value)
     bool first = true;
-    floatx16 sacc[2];  // S^T of the current tile, as (score - running max)
+    floatx16 sacc[2];  // S^T of the current tile, as (score - m_run)
     u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
 
-    // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of
-    // phases, the second group one phase behind.  A wave's phases alternate
+    // Ping-pong: a wave's phases alternate
     //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
     //   S(j): softmax of tile j                     (VALU)
-    // so on every SIMD one wave keeps the matrix core busy while the other does its
-    // softmax.  Each phase ends with a workgroup barrier.  Tile j sits in LDS stage
-    // j % 4 from two tiles before its first use (S^T in M(j)) until its last (PV in
-    // M(j+1) of the trailing group).
+    // Tile j sits in LDS stage j % 4 from two tiles before its first use (S^T in M(j))
+    // until its last (PV in M(j+1) of the trailing group).
     const int grp = wave >> 2;
-    const bool row_active = wave_valid;
+    auto tile_active = [&](int j) { return wave_valid && j * KT < kend_w; };
 
-    auto tile_active = [&](int j) { return row_active && j * KT < kend_w; };
+    // The operand reads of an M phase, x = 0 .. 31: x < 16 the V^T blocks of tile j-1
+    // (key group x/4, dim block x%4) from the V region at byte offset vso, x >= 16 the K
+    // blocks of tile j (head-dim step (x-16)/2, key block x%2) from the K region at kso.
+    auto rd = [&](int kso, int vso, int x) -> half8 {
+        if (x < 16)
+            return *reinterpret_cast<const half8 *>(vread + vso + vaddr[x & 3] + (x >> 2) * 2 * kHeadDim * 16);
+        const int y = x - 16;
+        return *reinterpret_cast<const half8 *>(kread + kso + kaddr[y >> 1] + (y & 1) * 32 * ROWB);
+    };
 
-    auto phase_m = [&](auto stg_c, int j) {
+    // MFMAs x0 .. x1-1 of the sequence above, each operand read RD MFMAs ahead.  With
+    // PRE the first RD reads were issued by the preceding softmax phase.
+    half8 buf[RD];
+    auto prefetch = [&](int vso) {
+#pragma unroll
+        for (int k = 0; k < RD; ++k)
+            buf[k] = rd(0, vso, k);
+    };
+    auto mstream = [&](auto x0_c, auto x1_c, auto pre_c, int kso, int vso) {
+        constexpr int X0 = decltype(x0_c)::value, X1 = decltype(x1_c)::value;
+        if (!decltype(pre_c)::value) {
+#pragma unroll
+            for (int k = 0; k < RD; ++k)
+                if (X0 + k < X1)
+                    buf[k] = rd(kso, vso, X0 + k);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = X0; x < X1; ++x) {
+            const half8 a = buf[(x - X0) % RD];
+            if (x < 16) {
+                o[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]),
+                                                                  o[x & 3], 0, 0, 0);
+            } else {
+                // the two key blocks' chains alternate, so consecutive MFMAs never wait
+                // on each other's results
+                const int y = x - 16, sb = y & 1;
+                sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[y >> 1], y < 2 ? mneg : sacc[sb], 0, 0, 0);
+            }
+            if (x + RD < X1)
+                buf[(x - X0) % RD] = rd(kso, vso, x + RD);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Tile staging for M(j) (STG = j % 4): tile j+1's V rows (loaded one phase pair ago)
+    // into its stage -- all of this wave's loads are complete afterwards, including its K
+    // share of tile j+1 -- then tile j+2's loads (V rows into registers, K straight into
+    // its stage).  It runs at the end of the softmax phase before M(j), while the SIMD
+    // partner is in its MFMA phase: the stages it writes were last read two phases ago.
+    auto stage_tiles = [&](auto stg_c, int j) {
         constexpr int STG = decltype(stg_c)::value;
-        const char *st = STG == 0 ? lds_st0 : (STG == 1 ? lds_st1 : (STG == 2 ? lds_st2 : lds_st3));
-        const char *stp = STG == 0 ? lds_st3 : (STG == 1 ? lds_st0 : (STG == 2 ? lds_st1 : lds_st2));
-        char *st2 = STG == 0 ? lds_st2 : (STG == 1 ? lds_st3 : (STG == 2 ? lds_st0 : lds_st1));
-        char *st1 = STG == 0 ? lds_st1 : (STG == 1 ? lds_st2 : (STG == 2 ? lds_st3 : lds_st0));
-        // tile j+1: its V rows (loaded one phase pair ago) into its stage; all of this
-        // wave's loads are complete afterwards, including its K share of tile j+1
         if (j + 1 < ntiles) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            store_v(vr, st1, tid);
+            store_v<(STG + 1) % NSTAGE>(vr, lds, vst);
         }
-        // tile j+2: K straight into its stage, V rows into registers
-        // (V first: the compiler's own wait before reusing vr must not cover the K loads)
         if (j + 2 < ntiles) {
-            load_v(vr, vbase, (j + 2) * KT, kend - 1, tid);
-            dma_k(kbase, (j + 2) * KT, kend - 1, st2, wave, lane);
+            issue_v(vr, j + 2);
+            issue_k(j + 2, lds_base + (uint32_t)(((STG + 2) % NSTAGE) * TILE_B));
         }
+    };
+
+    // M(j), 1 <= j < ntiles: PV of tile j-1 and S^T of tile j.  A wave whose tile j-1 is
+    // past its last key runs it anyway on zero probabilities (its SIMD partner is in
+    // its softmax, so the matrix core is free), which keeps one code path.
+    auto phase_m = [&](auto stg_c, int j) {
+        constexpr int STG = decltype(stg_c)::value;
         // the matrix-core phase outranks the other group's softmax for issue slots
         __builtin_amdgcn_s_setprio(1);
-
-        // O^T += V^T . P^T for tile j-1: 16 MFMAs (key step g = 2 sb + s2, dim block db),
-        // V^T operands read four ahead
-        if (j >= 1 && tile_active(j - 1)) {
-            half8 vq[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                vq[x] = *reinterpret_cast<const half8 *>(stp + vaddr[x & 3] + (x >> 2) * 2 * kHeadDim * 16);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int gi = x >> 2, db = x & 3;
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vq[x & 3], __builtin_bit_cast(half8, pw[gi]),
-                                                               o[db], 0, 0, 0);
-                if (x + 4 < 16)
-                    vq[x & 3] = *reinterpret_cast<const half8 *>(stp + vaddr[(x + 4) & 3] +
-                                                                  ((x + 4) >> 2) * 2 * kHeadDim * 16);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        // S^T = K . Q^T for tile j: 16 MFMAs, K operands read four ahead; the
-        // accumulators start at -m_run so S^T leaves the MFMAs as (score - max)
-        if (j < ntiles && tile_active(j)) {
-            // the two key blocks' accumulation chains alternate, so consecutive MFMAs
-            // never wait on each other's results
-            half8 kq[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                kq[x] = *reinterpret_cast<const half8 *>(st + kaddr[x >> 1] + (x & 1) * 32 * ROWB);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int x = 0; x < 16; ++x) {
-                const int sb = x & 1, s = x >> 1;
-                sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    kq[x & 3], qop[s], s == 0 ? floatx16(-m_run) : sacc[sb], 0, 0, 0);
-                if (x + 4 < 16)
-                    kq[x & 3] = *reinterpret_cast<const half8 *>(st + kaddr[(x + 4) >> 1] + ((x + 4) & 1) * 32 * ROWB);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{}, std::true_type{},
+                STG * TILE_B, ((STG + NSTAGE - 1) % NSTAGE) * TILE_B);
         __builtin_amdgcn_s_setprio(0);
         wg_barrier();
     };
 
-    auto phase_s = [&](int j) {
+    // probabilities of the tile (f16 pairs, the PV operand) and their sum
+    auto probs = [&]() -> float {
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 8 * (x & 1) + 2 * jj;
+                const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
+                                    __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
+                const half2v ph = __builtin_convertvector(pf, half2v);
+                pw[x][jj] = __builtin_bit_cast(uint32_t, ph);
+                if (jj & 1)
+                    ls1 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls1, false);
+                else
+                    ls0 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls0, false);
+            }
+        }
+        return ls0 + ls1;
+    };
+    // move the reference max up to the tile's row max (exact path)
+    auto move_max = [&](bool init) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, sacc[sb][r]);
+        }
+        mx = half_max(mx);
+        const float d = init ? mx : fmaxf(mx, 0.f);
+        if (!init) {
+            const float alpha = __builtin_amdgcn_exp2f(-d);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                o[db] *= alpha;
+        }
+        m_run += d;
+        mneg = floatx16(-m_run);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sacc[sb][r] -= d;
+        }
+    };
+
+    // S(j) (STG = j % 4): softmax of tile j, then the staging and the first operand
+    // reads (V^T of tile j) of M(j+1).
+    auto phase_s = [&](auto stg_c, int j) {
+        constexpr int STG = decltype(stg_c)::value;
         if (tile_active(j)) {
             const int kb = j * KT;
             // causal mask (only on tiles reaching past the block's first query)
@@ -389,80 +515,62 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                     }
                 }
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, sacc[sb][r]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32)); // max over the tile of (score - m_run)
-            // The first tile sets the max exactly; later tiles move it (and rescale the
-            // accumulators) only when some lane's max grows by more than 2^8.
-            if (first || __any(mx > RESCALE_LOG2)) {
-                const float d = first ? mx : fmaxf(mx, 0.f);
-                const float alpha = __builtin_amdgcn_exp2f(-d);
-                if (!first) {
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        o[db] *= alpha;
-                }
-                m_run += d;
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        sacc[sb][r] -= d;
-                }
+            if (first) {
+                move_max(true); // a row's first tile holds key 0, visible to every row
                 first = false;
             }
-            // probabilities, packed to f16 pairs (the PV operand) and summed as used
-            float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 8 * (x & 1) + 2 * jj;
-                    const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
-                                        __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
-                    const half2v ph = __builtin_convertvector(pf, half2v);
-                    pw[x][jj] = __builtin_bit_cast(uint32_t, ph);
-                    if (jj & 1)
-                        ls1 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls1, false);
-                    else
-                        ls0 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls0, false);
-                }
+            float lt = probs();
+            if (__builtin_amdgcn_ballot_w64(!(lt <= 3.0e38f))) {
+                move_max(false);
+                lt = probs();
             }
-            l_run += ls0 + ls1;
+            l_run += lt;
+        } else {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                pw[x] = u32x4{0u};
         }
+        stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
+        prefetch(STG * TILE_B);
         wg_barrier();
     };
 
     if (grp == 1)
         wg_barrier(); // the trailing group starts one phase late
-    for (int j0 = 0; j0 <= ntiles; j0 += 4) {
-        phase_m(std::integral_constant<int, 0>{}, j0);
-        if (j0 < ntiles) {
-            phase_s(j0);
-            phase_m(std::integral_constant<int, 1>{}, j0 + 1);
-            if (j0 + 1 < ntiles) {
-                phase_s(j0 + 1);
-                phase_m(std::integral_constant<int, 2>{}, j0 + 2);
-                if (j0 + 2 < ntiles) {
-                    phase_s(j0 + 2);
-                    phase_m(std::integral_constant<int, 3>{}, j0 + 3);
-                    if (j0 + 3 < ntiles)
-                        phase_s(j0 + 3);
+    // M(0): S^T of tile 0 only
+    stage_tiles(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_s_setprio(1);
+    mstream(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{}, std::false_type{}, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    wg_barrier();
+    phase_s(std::integral_constant<int, 0>{}, 0);
+    for (int j0 = 1; j0 < ntiles; j0 += 4) {
+        phase_m(std::integral_constant<int, 1>{}, j0);
+        phase_s(std::integral_constant<int, 1>{}, j0);
+        if (j0 + 1 < ntiles) {
+            phase_m(std::integral_constant<int, 2>{}, j0 + 1);
+            phase_s(std::integral_constant<int, 2>{}, j0 + 1);
+            if (j0 + 2 < ntiles) {
+                phase_m(std::integral_constant<int, 3>{}, j0 + 2);
+                phase_s(std::integral_constant<int, 3>{}, j0 + 2);
+                if (j0 + 3 < ntiles) {
+                    phase_m(std::integral_constant<int, 0>{}, j0 + 3);
+                    phase_s(std::integral_constant<int, 0>{}, j0 + 3);
                 }
             }
         }
     }
+    // M(ntiles): PV of the last tile only (its first reads were issued by S(ntiles-1))
+    __builtin_amdgcn_s_setprio(1);
+    mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{}, std::true_type{}, 0,
+            ((ntiles - 1) % NSTAGE) * TILE_B);
+    __builtin_amdgcn_s_setprio(0);
+    wg_barrier();
     if (grp == 0)
         wg_barrier(); // same barrier count for both groups
 
     // ---- normalise and write: lane holds dims 32db + 8*(r/4) + 4*hh + r%4 of query c
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = half_sum(l_run);
     const float inv = 1.f / l_tot;
     if (row_valid) {
         uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
