@@ -11,9 +11,9 @@
 //
 // Work decomposition.  For one (unit, KV head) the work items are (block of 32 new
 // tokens, query head of the group), numbered token-block-major.  A workgroup of 8 waves
-// takes 8 consecutive items (one per wave), so it spans few adjacent token blocks and
-// shares every K/V tile it stages in LDS among 8 x 32 query rows.  Per 64-key tile a
-// wave issues 32 MFMAs (v_mfma_f32_32x32x16_f16):
+// takes a work unit of 8 consecutive items (one per wave), so it spans few adjacent
+// token blocks and shares every K/V tile it stages in LDS among 8 x 32 query rows.  Per
+// 64-key tile a wave issues 32 MFMAs (v_mfma_f32_32x32x16_f16):
 //   S^T (64 keys x 32 queries) = K . Q^T        -- 2 key blocks x 8 head-dim steps
 //   O^T (128 dims x 32 queries) += V^T . P^T    -- 2 key blocks x 2 key steps x 4 dim blocks
 // Working on S^T puts one query in each lane (lane l: query l % 32, half l / 32), so the
@@ -52,14 +52,19 @@
 //           thread) one phase pair before they are written.
 // Tile loads use a wave-uniform tile base address plus per-lane 32-bit offsets fixed for
 // the whole kernel; only a workgroup's last, partial tile clamps rows to the last key.
-// Grid order: heavier (later) work first; when the number of (unit, KV head) pairs is a
-// multiple of 8, all workgroups of one pair go to the same XCD (workgroups are dealt to
-// the 8 XCDs round-robin) so its K/V stays in that XCD's L2.
+// Persistent grid: one workgroup per compute unit loops over the work units (8 items
+// each), heavier (later) units first, in a snake order that evens out the rounds and
+// keeps every unit of a (unit, KV head) pair on one XCD when the counts allow it.  A
+// workgroup's next unit starts while the previous one's output stores drain, with no
+// workgroup launch in between.  Outputs leave through LDS so that each global store
+// writes whole 256-byte rows.
 #include "device_common.h"
 #include "launch.h"
 
 #include <math.h>
+#include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace kvrope {
@@ -86,8 +91,9 @@ struct PrefillParams {
     int n, t, hq, hkv, s_cap, max_hist;
     int G;       // query heads per KV head
     int items;   // tblocks * G work items per (unit, KV head)
-    int wpk;     // workgroups per (unit, KV head) = ceil(items / 8)
-    int xcd;     // XCD-aware block mapping
+    int wpk;     // work units per (unit, KV head) = ceil(items / 8)
+    int units;   // work units in all: n * hkv * wpk
+    int xcd;     // grid size is a multiple of 8 (XCD-preserving snake order)
     float scale_log2;
 };
 
@@ -197,393 +203,429 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     const int lane = tid & 63;
     const int c = lane & 31;  // query within the wave's block (S^T column)
     const int hh = lane >> 5; // lane half
-
-    // ---- block -> (unit, KV head, workgroup rank); heavier workgroups first
     const int KP = p.n * p.hkv;
-    int kp, rank;
-    const int b = blockIdx.x;
-    if (p.xcd) {
-        const int x = b & 7, slot = b >> 3;
-        const int per_x = KP >> 3;
-        rank = slot / per_x;
-        kp = x + 8 * (slot - rank * per_x);
-    } else {
-        rank = b / KP;
-        kp = b - rank * KP;
-    }
-    const int wk = p.wpk - 1 - rank;
-    const int u = kp / p.hkv, g = kp - u * p.hkv;
-    const int item = wk * NW + wave;
-    const bool wave_valid = item < p.items;
-    const int last_item = min(wk * NW + NW - 1, p.items - 1);
-    const int my_item = wave_valid ? item : last_item;
-    const int tb = my_item / p.G;
-    const int h = g * p.G + (my_item - tb * p.G);
-    const int i0 = tb * QB;
-    const int i = i0 + c;
-    const bool row_valid = wave_valid && i < p.t;
 
-    const int hist = p.lens ? p.lens[u] : 0;
-    if (hist < 0 || hist > p.max_hist) {
-        // invalid history length: no cache was written for this unit; report NaN
-        if (row_valid && hh == 0) {
-            uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
-            for (int d = 0; d < kHeadDim; ++d)
-                orow[d] = qnan16();
-        }
-        return;
-    }
-    const int tb_last = last_item / p.G;
-    const int kend = hist + min((tb_last + 1) * QB, p.t); // keys the workgroup needs
-    const int klast = kend - 1;
-    const int ntiles = (kend + KT - 1) / KT;
-    const int kend_w = hist + min(i0 + QB, p.t);        // keys this wave needs
-    const int qlimit = hist + i;                         // last visible key of the lane's query
+    // Persistent workgroups.  Work unit v (0 .. units-1) is (KV pair v % KP, rank v / KP);
+    // rank 0 is the heaviest (the last token blocks).  Round r hands unit r * P + w' to
+    // workgroup w, with w' = w on even rounds and reversed on odd ones, so the cost of
+    // consecutive rounds evens out.  With P a multiple of 8 the reversal keeps w' = w
+    // (mod 8): workgroups are dealt to the 8 XCDs round-robin, so when KP is a multiple
+    // of 8 too, every unit of a pair runs on the same XCD and its K/V stays in that L2.
+    const int P = gridDim.x;
 
-    const char *kbase = reinterpret_cast<const char *>(p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
-    const char *vbase = reinterpret_cast<const char *>(p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
-
-    // per-lane tile offsets (full tiles) and the LDS addresses of this thread
-    uint32_t koff[2], voff[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        koff[r] = koffset(krow(wave, lane, r), lane);
-        voff[r] = voffset(vkey(tid, r), tid);
-    }
-    const uint32_t lds_base = lds_offset(lds);
-    uint32_t vst[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        vst[e] = vstore_offset(tid, e);
-
-    // Tile loads.  Rows at or past kend clamp to the last key (finite values; they are
-    // masked or carry probability 0), and only the last tile can hold such rows.
-    auto issue_k = [&](int j, uint32_t stage_lds) {
-        const int kb = j * KT;
-        const char *tile = kbase + (int64_t)kb * ROWB;
-        if (kb + KT <= kend) {
-            dma_k(tile, koff, stage_lds, wave);
-        } else {
-            // the source row clamps; the swizzled chunk stays the destination row's
-            uint32_t o[2];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int row = krow(wave, lane, r);
-                o[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
-            }
-            dma_k(tile, o, stage_lds, wave);
-        }
-    };
-    auto issue_v = [&](VRegs &r, int j) {
-        const int kb = j * KT;
-        // (readfirstlane keeps the whole tile offset in the scalar base address)
-        const char *tile = vbase + (int64_t)__builtin_amdgcn_readfirstlane(kb) * ROWB;
-        if (kb + KT <= kend) {
-            load_v(r, tile, voff);
-        } else {
-            uint32_t o[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                o[x] = voffset(min(vkey(tid, x), klast - kb), tid);
-            load_v(r, tile, o);
-        }
-    };
-
-    // ---- loads in flight, oldest first: rotation table, this lane's q row, tiles 0 and 1
-    const int dp_t = tid & (kMaxPairs - 1);
-    const bool rot_t = 2 * dp_t >= tab.off;
-    const double wr = tab.wrev[rot_t ? dp_t - (tab.off >> 1) : 0];
-    // rows past t read row t-1 (branch-free loads; their outputs are never written)
-    const int iq = min(i, p.t - 1);
-    const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
-    const int qpos = p.pos[(int64_t)u * p.t + iq];
-    u32x4 qin[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        qin[s] = ld16(qrow + 16 * s + 8 * hh);
-    issue_k(0, lds_base);
-    if (ntiles > 1)
-        issue_k(1, lds_base + TILE_B);
-    VRegs vr;
-    issue_v(vr, 0);
-    const float sl2 = p.scale_log2;
+    // rotation tables, shared by every unit
     if (tid < kMaxPairs) {
-        wdim[tid] = rot_t ? wr : 0.0;
+        const bool rot_t = 2 * tid >= tab.off;
+        const float sl2 = p.scale_log2;
+        wdim[tid] = rot_t ? tab.wrev[tid - (tab.off >> 1)] : 0.0;
         sdim[tid] = rot_t ? (float)tab.mscale * sl2 : sl2;
     }
     wg_barrier();
 
-    // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16
-    half8 qop[8];
-    {
-        const double posd = (double)qpos;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int dp0 = 8 * s + 4 * hh;
-            const u32x4 in = qin[s];
-            u32x4 hv;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp0 + m]);
-                const float sc = sdim[dp0 + m];
-                const float cs = __builtin_amdgcn_cosf(rf) * sc;
-                const float sn = __builtin_amdgcn_sinf(rf) * sc;
-                const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
-                const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
-                hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
+    for (int round = 0;; ++round) {
+        int slot = blockIdx.x;
+        if (round & 1)
+            slot = p.xcd ? ((P >> 3) - 1 - (slot >> 3)) * 8 + (slot & 7) : P - 1 - slot;
+        const int v = round * P + slot;
+        if (v >= p.units)
+            break;
+        const int rank = v / KP;
+        const int kp = v - rank * KP;
+        const int wk = p.wpk - 1 - rank;
+        const int u = kp / p.hkv, g = kp - u * p.hkv;
+        const int item = wk * NW + wave;
+        const bool wave_valid = item < p.items;
+        const int last_item = min(wk * NW + NW - 1, p.items - 1);
+        const int my_item = wave_valid ? item : last_item;
+        const int tb = my_item / p.G;
+        const int h = g * p.G + (my_item - tb * p.G);
+        const int i0 = tb * QB;
+        const int i = i0 + c;
+        const bool row_valid = wave_valid && i < p.t;
+
+        const int hist = p.lens ? p.lens[u] : 0;
+        if (hist < 0 || hist > p.max_hist) {
+            // invalid history length: no cache was written for this unit; report NaN
+            if (row_valid && hh == 0) {
+                uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
+                for (int d = 0; d < kHeadDim; ++d)
+                    orow[d] = qnan16();
             }
-            qop[s] = __builtin_bit_cast(half8, hv);
+            continue; // uniform over the workgroup: hist belongs to the unit
         }
-    }
+        const int tb_last = last_item / p.G;
+        const int kend = hist + min((tb_last + 1) * QB, p.t); // keys the workgroup needs
+        const int klast = kend - 1;
+        const int ntiles = (kend + KT - 1) / KT;
+        const int kend_w = hist + min(i0 + QB, p.t);        // keys this wave needs
+        const int qlimit = hist + i;                         // last visible key of the lane's query
 
-    // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
-    const char *kread = lds + c * ROWB;
-    int kaddr[8];
+        const char *kbase = reinterpret_cast<const char *>(p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
+        const char *vbase = reinterpret_cast<const char *>(p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
+
+        // per-lane tile offsets (full tiles) and the LDS addresses of this thread
+        uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-        kaddr[s] = ((2 * s + hh) ^ kswz(c)) << 4;
-    const char *vread = lds + VREG_B + hh * kHeadDim * 16;
-    int vaddr[4];
+        for (int r = 0; r < 2; ++r) {
+            koff[r] = koffset(krow(wave, lane, r), lane);
+            voff[r] = voffset(vkey(tid, r), tid);
+        }
+        const uint32_t lds_base = lds_offset(lds);
+        uint32_t vst[8];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-        vaddr[db] = vpos(32 * db + c) * 16;
+        for (int e = 0; e < 8; ++e)
+            vst[e] = vstore_offset(tid, e);
 
-    // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    store_v<0>(vr, lds, vst);
-    if (ntiles > 1)
-        issue_v(vr, 1);
-    wg_barrier();
-
-    floatx16 o[4];
+        // Tile loads.  Rows at or past kend clamp to the last key (finite values; they are
+        // masked or carry probability 0), and only the last tile can hold such rows.
+        auto issue_k = [&](int j, uint32_t stage_lds) {
+            const int kb = j * KT;
+            const char *tile = kbase + (int64_t)kb * ROWB;
+            if (kb + KT <= kend) {
+                dma_k(tile, koff, stage_lds, wave);
+            } else {
+                // the source row clamps; the swizzled chunk stays the destination row's
+                uint32_t o[2];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-        o[db] = floatx16{0.f};
-    // reference max (log2 units) and the running sum of the f16 probabilities
-    float m_run = 0.f, l_run = 0.f;
-    floatx16 mneg = floatx16{0.f}; // -m_run in every accumulator slot (S^T start value)
-    bool first = true;
-    floatx16 sacc[2];  // S^T of the current tile, as (score - m_run)
-    u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
-
-    // Ping-pong: a wave's phases alternate
-    //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
-    //   S(j): softmax of tile j                     (VALU)
-    // Tile j sits in LDS stage j % 4 from two tiles before its first use (S^T in M(j))
-    // until its last (PV in M(j+1) of the trailing group).
-    const int grp = wave >> 2;
-    auto tile_active = [&](int j) { return wave_valid && j * KT < kend_w; };
-
-    // The operand reads of an M phase, x = 0 .. 31: x < 16 the V^T blocks of tile j-1
-    // (key group x/4, dim block x%4) from the V region at byte offset vso, x >= 16 the K
-    // blocks of tile j (head-dim step (x-16)/2, key block x%2) from the K region at kso.
-    auto rd = [&](int kso, int vso, int x) -> half8 {
-        if (x < 16)
-            return *reinterpret_cast<const half8 *>(vread + vso + vaddr[x & 3] + (x >> 2) * 2 * kHeadDim * 16);
-        const int y = x - 16;
-        return *reinterpret_cast<const half8 *>(kread + kso + kaddr[y >> 1] + (y & 1) * 32 * ROWB);
-    };
-
-    // MFMAs x0 .. x1-1 of the sequence above, each operand read RD MFMAs ahead.  With
-    // PRE the first RD reads were issued by the preceding softmax phase.
-    half8 buf[RD];
-    auto prefetch = [&](int vso) {
+                for (int r = 0; r < 2; ++r) {
+                    const int row = krow(wave, lane, r);
+                    o[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
+                }
+                dma_k(tile, o, stage_lds, wave);
+            }
+        };
+        auto issue_v = [&](VRegs &r, int j) {
+            const int kb = j * KT;
+            // (readfirstlane keeps the whole tile offset in the scalar base address)
+            const char *tile = vbase + (int64_t)__builtin_amdgcn_readfirstlane(kb) * ROWB;
+            if (kb + KT <= kend) {
+                load_v(r, tile, voff);
+            } else {
+                uint32_t o[2];
 #pragma unroll
-        for (int k = 0; k < RD; ++k)
-            buf[k] = rd(0, vso, k);
-    };
-    auto mstream = [&](auto x0_c, auto x1_c, auto pre_c, int kso, int vso) {
-        constexpr int X0 = decltype(x0_c)::value, X1 = decltype(x1_c)::value;
-        if (!decltype(pre_c)::value) {
+                for (int x = 0; x < 2; ++x)
+                    o[x] = voffset(min(vkey(tid, x), klast - kb), tid);
+                load_v(r, tile, o);
+            }
+        };
+
+        // ---- loads in flight: this lane's q row, tiles 0 and 1
+        // rows past t read row t-1 (branch-free loads; their outputs are never written)
+        const int iq = min(i, p.t - 1);
+        const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
+        const int qpos = p.pos[(int64_t)u * p.t + iq];
+        u32x4 qin[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            qin[s] = ld16(qrow + 16 * s + 8 * hh);
+        issue_k(0, lds_base);
+        if (ntiles > 1)
+            issue_k(1, lds_base + TILE_B);
+        VRegs vr;
+        issue_v(vr, 0);
+
+        // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16
+        half8 qop[8];
+        {
+            const double posd = (double)qpos;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int dp0 = 8 * s + 4 * hh;
+                const u32x4 in = qin[s];
+                u32x4 hv;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp0 + m]);
+                    const float sc = sdim[dp0 + m];
+                    const float cs = __builtin_amdgcn_cosf(rf) * sc;
+                    const float sn = __builtin_amdgcn_sinf(rf) * sc;
+                    const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
+                    const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
+                    hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
+                }
+                qop[s] = __builtin_bit_cast(half8, hv);
+            }
+        }
+
+        // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
+        const char *kread = lds + c * ROWB;
+        int kaddr[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            kaddr[s] = ((2 * s + hh) ^ kswz(c)) << 4;
+        const char *vread = lds + VREG_B + hh * kHeadDim * 16;
+        int vaddr[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            vaddr[db] = vpos(32 * db + c) * 16;
+
+        // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        store_v<0>(vr, lds, vst);
+        if (ntiles > 1)
+            issue_v(vr, 1);
+        wg_barrier();
+
+        floatx16 o[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            o[db] = floatx16{0.f};
+        // reference max (log2 units) and the running sum of the f16 probabilities
+        float m_run = 0.f, l_run = 0.f;
+        floatx16 mneg = floatx16{0.f}; // -m_run in every accumulator slot (S^T start value)
+        bool first = true;
+        floatx16 sacc[2];  // S^T of the current tile, as (score - m_run)
+        u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
+
+        // Ping-pong: a wave's phases alternate
+        //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
+        //   S(j): softmax of tile j                     (VALU)
+        // Tile j sits in LDS stage j % 4 from two tiles before its first use (S^T in M(j))
+        // until its last (PV in M(j+1) of the trailing group).
+        const int grp = wave >> 2;
+        auto tile_active = [&](int j) { return wave_valid && j * KT < kend_w; };
+
+        // The operand reads of an M phase, x = 0 .. 31: x < 16 the V^T blocks of tile j-1
+        // (key group x/4, dim block x%4) from the V region at byte offset vso, x >= 16 the K
+        // blocks of tile j (head-dim step (x-16)/2, key block x%2) from the K region at kso.
+        auto rd = [&](int kso, int vso, int x) -> half8 {
+            if (x < 16)
+                return *reinterpret_cast<const half8 *>(vread + vso + vaddr[x & 3] + (x >> 2) * 2 * kHeadDim * 16);
+            const int y = x - 16;
+            return *reinterpret_cast<const half8 *>(kread + kso + kaddr[y >> 1] + (y & 1) * 32 * ROWB);
+        };
+
+        // MFMAs x0 .. x1-1 of the sequence above, each operand read RD MFMAs ahead.  With
+        // PRE the first RD reads were issued by the preceding softmax phase.
+        half8 buf[RD];
+        auto prefetch = [&](int vso) {
 #pragma unroll
             for (int k = 0; k < RD; ++k)
-                if (X0 + k < X1)
-                    buf[k] = rd(kso, vso, X0 + k);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+                buf[k] = rd(0, vso, k);
+        };
+        auto mstream = [&](auto x0_c, auto x1_c, auto pre_c, int kso, int vso) {
+            constexpr int X0 = decltype(x0_c)::value, X1 = decltype(x1_c)::value;
+            if (!decltype(pre_c)::value) {
 #pragma unroll
-        for (int x = X0; x < X1; ++x) {
-            const half8 a = buf[(x - X0) % RD];
-            if (x < 16) {
-                o[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]),
-                                                                  o[x & 3], 0, 0, 0);
-            } else {
-                // the two key blocks' chains alternate, so consecutive MFMAs never wait
-                // on each other's results
-                const int y = x - 16, sb = y & 1;
-                sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[y >> 1], y < 2 ? mneg : sacc[sb], 0, 0, 0);
+                for (int k = 0; k < RD; ++k)
+                    if (X0 + k < X1)
+                        buf[k] = rd(kso, vso, X0 + k);
             }
-            if (x + RD < X1)
-                buf[(x - X0) % RD] = rd(kso, vso, x + RD);
             __builtin_amdgcn_sched_barrier(0);
-        }
-    };
+#pragma unroll
+            for (int x = X0; x < X1; ++x) {
+                const half8 a = buf[(x - X0) % RD];
+                if (x < 16) {
+                    o[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]),
+                                                                      o[x & 3], 0, 0, 0);
+                } else {
+                    // the two key blocks' chains alternate, so consecutive MFMAs never wait
+                    // on each other's results
+                    const int y = x - 16, sb = y & 1;
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[y >> 1], y < 2 ? mneg : sacc[sb], 0, 0, 0);
+                }
+                if (x + RD < X1)
+                    buf[(x - X0) % RD] = rd(kso, vso, x + RD);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
 
-    // Tile staging for M(j) (STG = j % 4): tile j+1's V rows (loaded one phase pair ago)
-    // into its stage -- all of this wave's loads are complete afterwards, including its K
-    // share of tile j+1 -- then tile j+2's loads (V rows into registers, K straight into
-    // its stage).  It runs at the end of the softmax phase before M(j), while the SIMD
-    // partner is in its MFMA phase: the stages it writes were last read two phases ago.
-    auto stage_tiles = [&](auto stg_c, int j) {
-        constexpr int STG = decltype(stg_c)::value;
-        if (j + 1 < ntiles) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            store_v<(STG + 1) % NSTAGE>(vr, lds, vst);
-        }
-        if (j + 2 < ntiles) {
-            issue_v(vr, j + 2);
-            issue_k(j + 2, lds_base + (uint32_t)(((STG + 2) % NSTAGE) * TILE_B));
-        }
-    };
+        // Tile staging for M(j) (STG = j % 4): tile j+1's V rows (loaded one phase pair ago)
+        // into its stage -- all of this wave's loads are complete afterwards, including its K
+        // share of tile j+1 -- then tile j+2's loads (V rows into registers, K straight into
+        // its stage).  It runs at the end of the softmax phase before M(j), while the SIMD
+        // partner is in its MFMA phase: the stages it writes were last read two phases ago.
+        auto stage_tiles = [&](auto stg_c, int j) {
+            constexpr int STG = decltype(stg_c)::value;
+            if (j + 1 < ntiles) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                store_v<(STG + 1) % NSTAGE>(vr, lds, vst);
+            }
+            if (j + 2 < ntiles) {
+                issue_v(vr, j + 2);
+                issue_k(j + 2, lds_base + (uint32_t)(((STG + 2) % NSTAGE) * TILE_B));
+            }
+        };
 
-    // M(j), 1 <= j < ntiles: PV of tile j-1 and S^T of tile j.  A wave whose tile j-1 is
-    // past its last key runs it anyway on zero probabilities (its SIMD partner is in
-    // its softmax, so the matrix core is free), which keeps one code path.
-    auto phase_m = [&](auto stg_c, int j) {
-        constexpr int STG = decltype(stg_c)::value;
-        // the matrix-core phase outranks the other group's softmax for issue slots
+        // M(j), 1 <= j < ntiles: PV of tile j-1 and S^T of tile j.  A wave whose tile j-1 is
+        // past its last key runs it anyway on zero probabilities (its SIMD partner is in
+        // its softmax, so the matrix core is free), which keeps one code path.
+        auto phase_m = [&](auto stg_c, int j) {
+            constexpr int STG = decltype(stg_c)::value;
+            // the matrix-core phase outranks the other group's softmax for issue slots
+            __builtin_amdgcn_s_setprio(1);
+            mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{}, std::true_type{},
+                    STG * TILE_B, ((STG + NSTAGE - 1) % NSTAGE) * TILE_B);
+            __builtin_amdgcn_s_setprio(0);
+            wg_barrier();
+        };
+
+        // probabilities of the tile (f16 pairs, the PV operand) and their sum
+        auto probs = [&]() -> float {
+            float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 8 * (x & 1) + 2 * jj;
+                    const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
+                                        __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
+                    const half2v ph = __builtin_convertvector(pf, half2v);
+                    pw[x][jj] = __builtin_bit_cast(uint32_t, ph);
+                    if (jj & 1)
+                        ls1 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls1, false);
+                    else
+                        ls0 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls0, false);
+                }
+            }
+            return ls0 + ls1;
+        };
+        // move the reference max up to the tile's row max (exact path)
+        auto move_max = [&](bool init) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, sacc[sb][r]);
+            }
+            mx = half_max(mx);
+            const float d = init ? mx : fmaxf(mx, 0.f);
+            if (!init) {
+                const float alpha = __builtin_amdgcn_exp2f(-d);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    o[db] *= alpha;
+            }
+            m_run += d;
+            mneg = floatx16(-m_run);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sacc[sb][r] -= d;
+            }
+        };
+
+        // S(j) (STG = j % 4): softmax of tile j, then the staging and the first operand
+        // reads (V^T of tile j) of M(j+1).
+        auto phase_s = [&](auto stg_c, int j) {
+            constexpr int STG = decltype(stg_c)::value;
+            if (tile_active(j)) {
+                const int kb = j * KT;
+                // causal mask (only on tiles reaching past the block's first query)
+                if (kb + KT - 1 > hist + i0) {
+                    const int lim = qlimit - kb - 4 * hh;
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            if (32 * sb + 8 * (r >> 2) + (r & 3) > lim)
+                                sacc[sb][r] = -INFINITY;
+                        }
+                    }
+                }
+                if (first) {
+                    move_max(true); // a row's first tile holds key 0, visible to every row
+                    first = false;
+                }
+                float lt = probs();
+                if (__builtin_amdgcn_ballot_w64(!(lt <= 3.0e38f))) {
+                    move_max(false);
+                    lt = probs();
+                }
+                l_run += lt;
+            } else {
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    pw[x] = u32x4{0u};
+            }
+            stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
+            prefetch(STG * TILE_B);
+            wg_barrier();
+        };
+
+        if (grp == 1)
+            wg_barrier(); // the trailing group starts one phase late
+        // M(0): S^T of tile 0 only
+        stage_tiles(std::integral_constant<int, 0>{}, 0);
         __builtin_amdgcn_s_setprio(1);
-        mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{}, std::true_type{},
-                STG * TILE_B, ((STG + NSTAGE - 1) % NSTAGE) * TILE_B);
+        mstream(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{}, std::false_type{}, 0, 0);
         __builtin_amdgcn_s_setprio(0);
         wg_barrier();
-    };
-
-    // probabilities of the tile (f16 pairs, the PV operand) and their sum
-    auto probs = [&]() -> float {
-        float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int r = 8 * (x & 1) + 2 * jj;
-                const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
-                                    __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
-                const half2v ph = __builtin_convertvector(pf, half2v);
-                pw[x][jj] = __builtin_bit_cast(uint32_t, ph);
-                if (jj & 1)
-                    ls1 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls1, false);
-                else
-                    ls0 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls0, false);
-            }
-        }
-        return ls0 + ls1;
-    };
-    // move the reference max up to the tile's row max (exact path)
-    auto move_max = [&](bool init) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                mx = fmaxf(mx, sacc[sb][r]);
-        }
-        mx = half_max(mx);
-        const float d = init ? mx : fmaxf(mx, 0.f);
-        if (!init) {
-            const float alpha = __builtin_amdgcn_exp2f(-d);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-                o[db] *= alpha;
-        }
-        m_run += d;
-        mneg = floatx16(-m_run);
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sacc[sb][r] -= d;
-        }
-    };
-
-    // S(j) (STG = j % 4): softmax of tile j, then the staging and the first operand
-    // reads (V^T of tile j) of M(j+1).
-    auto phase_s = [&](auto stg_c, int j) {
-        constexpr int STG = decltype(stg_c)::value;
-        if (tile_active(j)) {
-            const int kb = j * KT;
-            // causal mask (only on tiles reaching past the block's first query)
-            if (kb + KT - 1 > hist + i0) {
-                const int lim = qlimit - kb - 4 * hh;
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        if (32 * sb + 8 * (r >> 2) + (r & 3) > lim)
-                            sacc[sb][r] = -INFINITY;
+        phase_s(std::integral_constant<int, 0>{}, 0);
+        for (int j0 = 1; j0 < ntiles; j0 += 4) {
+            phase_m(std::integral_constant<int, 1>{}, j0);
+            phase_s(std::integral_constant<int, 1>{}, j0);
+            if (j0 + 1 < ntiles) {
+                phase_m(std::integral_constant<int, 2>{}, j0 + 1);
+                phase_s(std::integral_constant<int, 2>{}, j0 + 1);
+                if (j0 + 2 < ntiles) {
+                    phase_m(std::integral_constant<int, 3>{}, j0 + 2);
+                    phase_s(std::integral_constant<int, 3>{}, j0 + 2);
+                    if (j0 + 3 < ntiles) {
+                        phase_m(std::integral_constant<int, 0>{}, j0 + 3);
+                        phase_s(std::integral_constant<int, 0>{}, j0 + 3);
                     }
                 }
             }
-            if (first) {
-                move_max(true); // a row's first tile holds key 0, visible to every row
-                first = false;
-            }
-            float lt = probs();
-            if (__builtin_amdgcn_ballot_w64(!(lt <= 3.0e38f))) {
-                move_max(false);
-                lt = probs();
-            }
-            l_run += lt;
-        } else {
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                pw[x] = u32x4{0u};
         }
-        stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
-        prefetch(STG * TILE_B);
+        // M(ntiles): PV of the last tile only (its first reads were issued by S(ntiles-1))
+        __builtin_amdgcn_s_setprio(1);
+        mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{}, std::true_type{}, 0,
+                ((ntiles - 1) % NSTAGE) * TILE_B);
+        __builtin_amdgcn_s_setprio(0);
         wg_barrier();
-    };
+        if (grp == 0)
+            wg_barrier(); // same barrier count for both groups
 
-    if (grp == 1)
-        wg_barrier(); // the trailing group starts one phase late
-    // M(0): S^T of tile 0 only
-    stage_tiles(std::integral_constant<int, 0>{}, 0);
-    __builtin_amdgcn_s_setprio(1);
-    mstream(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{}, std::false_type{}, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    wg_barrier();
-    phase_s(std::integral_constant<int, 0>{}, 0);
-    for (int j0 = 1; j0 < ntiles; j0 += 4) {
-        phase_m(std::integral_constant<int, 1>{}, j0);
-        phase_s(std::integral_constant<int, 1>{}, j0);
-        if (j0 + 1 < ntiles) {
-            phase_m(std::integral_constant<int, 2>{}, j0 + 1);
-            phase_s(std::integral_constant<int, 2>{}, j0 + 1);
-            if (j0 + 2 < ntiles) {
-                phase_m(std::integral_constant<int, 3>{}, j0 + 2);
-                phase_s(std::integral_constant<int, 3>{}, j0 + 2);
-                if (j0 + 3 < ntiles) {
-                    phase_m(std::integral_constant<int, 0>{}, j0 + 3);
-                    phase_s(std::integral_constant<int, 0>{}, j0 + 3);
-                }
-            }
-        }
-    }
-    // M(ntiles): PV of the last tile only (its first reads were issued by S(ntiles-1))
-    __builtin_amdgcn_s_setprio(1);
-    mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{}, std::true_type{}, 0,
-            ((ntiles - 1) % NSTAGE) * TILE_B);
-    __builtin_amdgcn_s_setprio(0);
-    wg_barrier();
-    if (grp == 0)
-        wg_barrier(); // same barrier count for both groups
-
-    // ---- normalise and write: lane holds dims 32db + 8*(r/4) + 4*hh + r%4 of query c
-    const float l_tot = half_sum(l_run);
-    const float inv = 1.f / l_tot;
-    if (row_valid) {
-        uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
+        // ---- normalise and write.  The lane holds dims 32db + 8*(r/4) + 4*hh + r%4 of query
+        // c; the rows pass through the wave's own 8 KB slice of LDS stages 2-3 (idle from the
+        // last barrier until the next unit's first K tile 2 load, two barriers later), so
+        // that every global store writes whole 256-byte rows instead of 8-byte pieces of 64
+        // rows.  16-byte chunk k of row c sits at chunk k ^ (c % 16).
+        const float l_tot = half_sum(l_run);
+        const float inv = 1.f / l_tot;
+        char *ostage = lds + (wave < 4 ? 2 * TILE_B + wave * (QB * ROWB)
+                                       : VREG_B + 2 * TILE_B + (wave - 4) * (QB * ROWB));
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
                 const u32x2 w = {pack2h(o[db][4 * ig + 0] * inv, o[db][4 * ig + 1] * inv),
                                  pack2h(o[db][4 * ig + 2] * inv, o[db][4 * ig + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * ig + 4 * hh) = w;
+                const int chunk = (4 * db + ig) ^ (c & 15);
+                *reinterpret_cast<u32x2 *>(ostage + c * ROWB + chunk * 16 + hh * 8) = w;
             }
         }
-    }
+        // lanes read what other lanes wrote: keep the reads after the writes
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // Read back: lane L takes 16-byte chunk L % 16 of row 4x + L / 16.  With g = L / 16 the
+        // physical chunk is (L % 16) ^ g ^ 4 (x % 4), so row 4x's address is a per-lane base
+        // with bits 6-7 flipped by x % 4, plus 1 KB x.  All reads are issued before the
+        // first store; the asm statements keep the compiler from hoisting per-row values
+        // out of the unit loop (into spilled registers) or sinking reads into the stores'
+        // branches.
+        uint32_t rbase = (uint32_t)((ostage - lds) + (lane >> 4) * ROWB + (((lane & 15) ^ (lane >> 4)) << 4));
+        uint32_t olane = (uint32_t)((lane >> 4) * p.hq * ROWB + 16 * (lane & 15));
+        asm volatile("" : "+v"(rbase), "+v"(olane));
+        u32x4 orows[QB / 4];
+#pragma unroll
+        for (int x = 0; x < QB / 4; ++x) {
+            const uint32_t a = (rbase ^ (uint32_t)((x & 3) << 6)) + (uint32_t)(x * 4 * ROWB);
+            orows[x] = *reinterpret_cast<const u32x4 *>(lds + a);
+        }
+#pragma unroll
+        for (int x = 0; x < QB / 4; ++x)
+            asm volatile("" : "+v"(orows[x]));
+#pragma unroll
+        for (int x = 0; x < QB / 4; ++x) {
+            char *rows4 = reinterpret_cast<char *>(p.out + (((int64_t)u * p.t + i0 + 4 * x) * p.hq + h) * kHeadDim);
+            if (wave_valid && i0 + 4 * x + (lane >> 4) < p.t)
+                *reinterpret_cast<u32x4 *>(rows4 + olane) = orows[x];
+        }
+    } // work units
 }
 
 } // namespace
@@ -613,10 +655,20 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
     const int tblocks = (s.t + QB - 1) / QB;
     p.items = tblocks * p.G;
     p.wpk = (p.items + NW - 1) / NW;
-    const int KP = s.n * s.hkv;
-    p.xcd = (KP % 8 == 0) ? 1 : 0;
+    const int64_t units = (int64_t)s.n * s.hkv * p.wpk;
+    if (units > INT32_MAX)
+        return hipErrorInvalidValue;
+    p.units = (int)units;
     p.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
-    const int64_t blocks = (int64_t)KP * p.wpk;
+    // one workgroup per compute unit (the LDS ring takes most of a CU's LDS)
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    const int64_t blocks = std::min<int64_t>(units, std::max(ncu, 1));
+    p.xcd = (blocks % 8 == 0) ? 1 : 0;
 
     if (ev_before)
         (void)hipEventRecord(ev_before, stream);
