@@ -119,17 +119,28 @@ __device__ inline uint32_t koffset(int row, int lane)
     return (uint32_t)(row * ROWB + (((lane & 15) ^ kswz(row)) << 4));
 }
 
+// A wave-uniform pointer held in vector registers (e.g. an argument of a
+// non-inlined function), moved to scalar registers for the scalar base of a load.
+__device__ inline const char *uniform_ptr(const char *ptr)
+{
+    const uint64_t x = (uint64_t)(uintptr_t)ptr;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // K rows of one tile straight into an LDS stage.  `tile` is the wave-uniform address of
 // the tile's first row; the loads are inline asm so the compiler does not track them;
 // they are waited for explicitly (vmcnt) before the barrier that publishes the stage.
 __device__ inline void dma_k(const char *tile, const uint32_t (&off)[2], uint32_t stage_lds, int wave)
 {
+    const char *t = uniform_ptr(tile);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const uint32_t dst = stage_lds + (uint32_t)((8 * wave + 4 * i) * ROWB);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)((8 * wave + 4 * i) * ROWB));
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
-                     : "s"(dst), "v"(off[i]), "s"(tile)
+                     : "s"(dst), "v"(off[i]), "s"(t)
                      : "memory", "m0");
     }
 }
@@ -192,11 +203,164 @@ __device__ inline void store_v(const VRegs &r, char *lds, const uint32_t (&vst)[
     }
 }
 
+// q rotation: dims (2 dp, 2 dp + 1) of the lane's 8 dim steps (16 s + 8 hh .. + 7) by
+// fp32 trig of the fp64-reduced angle (revolutions wdim[dp] per position), scaled by
+// sdim[dp] and rounded to f16: the B operands of the S^T product.
+__device__ inline void rotate_q(half8 (&qop)[8], const u32x4 (&qin)[8], int qpos, int hh, const double *wdim,
+                                const float *sdim)
+{
+    const double posd = (double)qpos;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int dp0 = 8 * s + 4 * hh;
+        const u32x4 in = qin[s];
+        u32x4 hv;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp0 + m]);
+            const float sc = sdim[dp0 + m];
+            const float cs = __builtin_amdgcn_cosf(rf) * sc;
+            const float sn = __builtin_amdgcn_sinf(rf) * sc;
+            const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
+            const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
+            hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
+        }
+        qop[s] = __builtin_bit_cast(half8, hv);
+    }
+}
+
+// Rare path.  The fast path keeps each row's reference max from its first tile; when a
+// later key scores 2^16 or more above it, an f16 probability overflows and the row sum
+// turns infinite.  Then the whole workgroup recomputes the unit here with the running
+// max moved on every tile that exceeds it (so no probability exceeds 1): plainly, one
+// tile at a time through LDS stage 0, each wave its own item.  Not inlined, so that its
+// registers do not weigh on the fast path.
+__device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char *lds, const double *wdim,
+                                                     const float *sdim, int u, int g, int wk, int hist)
+{
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 31, hh = lane >> 5;
+    const int item = wk * NW + wave;
+    const bool wave_valid = item < p.items;
+    const int last_item = min(wk * NW + NW - 1, p.items - 1);
+    const int my_item = wave_valid ? item : last_item;
+    const int tb = my_item / p.G;
+    const int h = g * p.G + (my_item - tb * p.G);
+    const int i0 = tb * QB, i = i0 + c;
+    const int kend = hist + min((last_item / p.G + 1) * QB, p.t);
+    const int klast = kend - 1;
+    const int ntiles = (kend + KT - 1) / KT;
+    const int qlimit = hist + i;
+    const char *kbase = reinterpret_cast<const char *>(p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
+    const char *vbase = reinterpret_cast<const char *>(p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
+
+    const int iq = min(i, p.t - 1);
+    const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
+    u32x4 qin[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        qin[s] = ld16(qrow + 16 * s + 8 * hh);
+    half8 qop[8];
+    rotate_q(qop, qin, p.pos[(int64_t)u * p.t + iq], hh, wdim, sdim);
+
+    uint32_t vst[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        vst[e] = vstore_offset(tid, e);
+    floatx16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+        o[db] = floatx16{0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    for (int j = 0; j < ntiles; ++j) {
+        const int kb = j * KT;
+        // K rows (clamped past kend) straight into stage 0, V rows through registers
+        uint32_t ko[2], vo[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = krow(wave, lane, r);
+            ko[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
+            vo[r] = voffset(min(vkey(tid, r), klast - kb), tid);
+        }
+        dma_k(uniform_ptr(kbase + (int64_t)kb * ROWB), ko, __builtin_amdgcn_readfirstlane(lds_offset(lds)), wave);
+        VRegs vr;
+        load_v(vr, vbase + (int64_t)__builtin_amdgcn_readfirstlane(kb) * ROWB, vo);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        store_v<0>(vr, lds, vst);
+        wg_barrier();
+
+        floatx16 sacc[2] = {floatx16{0.f}, floatx16{0.f}};
+#pragma unroll
+        for (int y = 0; y < 16; ++y) {
+            const int sb = y & 1, st = y >> 1;
+            const half8 a = *reinterpret_cast<const half8 *>(lds + (32 * sb + c) * ROWB + (((2 * st + hh) ^ kswz(c)) << 4));
+            sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[st], sacc[sb], 0, 0, 0);
+        }
+        const int lim = qlimit - kb - 4 * hh;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (32 * sb + 8 * (r >> 2) + (r & 3) > lim)
+                    sacc[sb][r] = -INFINITY;
+                mx = fmaxf(mx, sacc[sb][r]);
+            }
+        }
+        mx = half_max(mx);
+        if (mx > m_run) {
+            // (the first tile holds key 0, visible to every row, so mx is finite)
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                o[db] *= alpha;
+            m_run = mx;
+        }
+        u32x4 pw[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 8 * (x & 1) + 2 * jj;
+                const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r] - m_run),
+                                    __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1] - m_run)};
+                l_run += pf[0] + pf[1];
+                pw[x][jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, half2v));
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int db = x & 3;
+            const half8 a = *reinterpret_cast<const half8 *>(lds + VREG_B + hh * kHeadDim * 16 +
+                                                             vpos(32 * db + c) * 16 + (x >> 2) * 2 * kHeadDim * 16);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]), o[db], 0, 0, 0);
+        }
+        wg_barrier(); // stage 0 is reloaded next
+    }
+    const float inv = 1.f / half_sum(l_run);
+    if (wave_valid && i < p.t) {
+        uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+                const u32x2 w = {pack2h(o[db][4 * ig + 0] * inv, o[db][4 * ig + 1] * inv),
+                                 pack2h(o[db][4 * ig + 2] * inv, o[db][4 * ig + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * ig + 4 * hh) = w;
+            }
+        }
+    }
+}
+
 __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab)
 {
     __shared__ __align__(16) char lds[2 * NSTAGE * TILE_B];
     __shared__ double wdim[kMaxPairs]; // revolutions per position of dim pair dp (0: unrotated)
     __shared__ float sdim[kMaxPairs];  // output scale of dim pair dp
+    __shared__ int ovf_unit;           // last unit whose row sums overflowed
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,6 +384,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         wdim[tid] = rot_t ? tab.wrev[tid - (tab.off >> 1)] : 0.0;
         sdim[tid] = rot_t ? (float)tab.mscale * sl2 : sl2;
     }
+    if (tid == 0)
+        ovf_unit = -1;
     wg_barrier();
 
     for (int round = 0;; ++round) {
@@ -326,56 +492,26 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 
         // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16
         half8 qop[8];
-        {
-            const double posd = (double)qpos;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int dp0 = 8 * s + 4 * hh;
-                const u32x4 in = qin[s];
-                u32x4 hv;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp0 + m]);
-                    const float sc = sdim[dp0 + m];
-                    const float cs = __builtin_amdgcn_cosf(rf) * sc;
-                    const float sn = __builtin_amdgcn_sinf(rf) * sc;
-                    const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
-                    const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
-                    hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
-                }
-                qop[s] = __builtin_bit_cast(half8, hv);
-            }
-        }
+        rotate_q(qop, qin, qpos, hh, wdim, sdim);
 
         // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
-        const char *kread = lds + c * ROWB;
-        int kaddr[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            kaddr[s] = ((2 * s + hh) ^ kswz(c)) << 4;
-        const char *vread = lds + VREG_B + hh * kHeadDim * 16;
-        int vaddr[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            vaddr[db] = vpos(32 * db + c) * 16;
-
-        // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        store_v<0>(vr, lds, vst);
-        if (ntiles > 1)
-            issue_v(vr, 1);
-        wg_barrier();
+        // K operand of head-dim step s: chunk (2s + hh) ^ (c % 16) of key row c.  The step
+        // sits in bits 5-7 of the byte offset, so one per-lane base serves all eight steps
+        // through an xor.  V^T operand of dim block db: dim row vpos(32 db + c) =
+        // 32 db + (c ^ (c / 8) ^ 4 (db % 2)), i.e. base ^ (64 (db % 2)) plus 512 db bytes.
+        const uint32_t kbase0 = (uint32_t)(c * ROWB + ((hh ^ kswz(c)) << 4));
+        const uint32_t vbase0 = (uint32_t)(VREG_B + hh * kHeadDim * 16 + 16 * (c ^ (c >> 3)));
 
         floatx16 o[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            o[db] = floatx16{0.f};
-        // reference max (log2 units) and the running sum of the f16 probabilities
-        float m_run = 0.f, l_run = 0.f;
-        floatx16 mneg = floatx16{0.f}; // -m_run in every accumulator slot (S^T start value)
+        // row sums of the f16 probabilities, accumulated on the matrix core (every slot of
+        // the lane holds the sum for its query)
+        floatx16 lsum;
+        float m_run = 0.f; // reference max (log2 units)
         bool first = true;
         floatx16 sacc[2];  // S^T of the current tile, as (score - m_run)
         u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
+        const half8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                            (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
 
         // Ping-pong: a wave's phases alternate
         //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
@@ -388,28 +524,41 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // The operand reads of an M phase, x = 0 .. 31: x < 16 the V^T blocks of tile j-1
         // (key group x/4, dim block x%4) from the V region at byte offset vso, x >= 16 the K
         // blocks of tile j (head-dim step (x-16)/2, key block x%2) from the K region at kso.
-        auto rd = [&](int kso, int vso, int x) -> half8 {
-            if (x < 16)
-                return *reinterpret_cast<const half8 *>(vread + vso + vaddr[x & 3] + (x >> 2) * 2 * kHeadDim * 16);
+        // (kb, vb: the per-lane bases, made opaque once per phase so that the compiler
+        // keeps two registers instead of hoisting twelve precomputed addresses)
+        auto rd = [&](uint32_t kb, uint32_t vb, int kso, int vso, int x) -> half8 {
+            if (x < 16) {
+                const int db = x & 3;
+                return *reinterpret_cast<const half8 *>(lds + ((vb ^ (uint32_t)(64 * (db & 1))) + 512 * db + vso +
+                                                               (x >> 2) * 2 * kHeadDim * 16));
+            }
             const int y = x - 16;
-            return *reinterpret_cast<const half8 *>(kread + kso + kaddr[y >> 1] + (y & 1) * 32 * ROWB);
+            return *reinterpret_cast<const half8 *>(lds + ((kb ^ (uint32_t)((y >> 1) << 5)) + kso + (y & 1) * 32 * ROWB));
         };
 
         // MFMAs x0 .. x1-1 of the sequence above, each operand read RD MFMAs ahead.  With
         // PRE the first RD reads were issued by the preceding softmax phase.
         half8 buf[RD];
         auto prefetch = [&](int vso) {
+            uint32_t kb = kbase0, vb = vbase0;
+            asm volatile("" : "+v"(kb), "+v"(vb));
 #pragma unroll
             for (int k = 0; k < RD; ++k)
-                buf[k] = rd(0, vso, k);
+                buf[k] = rd(kb, vb, 0, vso, k);
         };
         auto mstream = [&](auto x0_c, auto x1_c, auto pre_c, int kso, int vso) {
             constexpr int X0 = decltype(x0_c)::value, X1 = decltype(x1_c)::value;
+            uint32_t kb = kbase0, vb = vbase0;
+            asm volatile("" : "+v"(kb), "+v"(vb));
+            // the S^T chains start at -m: written into the (dead) S^T registers two slots per
+            // PV MFMA, or all at once when the phase has no PV part
+            float mr = -m_run;
+            asm volatile("" : "+v"(mr));
             if (!decltype(pre_c)::value) {
 #pragma unroll
                 for (int k = 0; k < RD; ++k)
                     if (X0 + k < X1)
-                        buf[k] = rd(kso, vso, X0 + k);
+                        buf[k] = rd(kb, vb, kso, vso, X0 + k);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -418,14 +567,26 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 if (x < 16) {
                     o[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]),
                                                                       o[x & 3], 0, 0, 0);
+                    // after the last dim block of key group x/4: its column sums
+                    if ((x & 3) == 3)
+                        lsum = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, __builtin_bit_cast(half8, pw[x >> 2]),
+                                                                      lsum, 0, 0, 0);
+                    if (X1 > 16) {
+                        sacc[x >> 3][2 * (x & 7)] = mr;
+                        sacc[x >> 3][2 * (x & 7) + 1] = mr;
+                    }
                 } else {
+                    if (x == 16 && X0 == 16) {
+                        sacc[0] = floatx16(mr);
+                        sacc[1] = floatx16(mr);
+                    }
                     // the two key blocks' chains alternate, so consecutive MFMAs never wait
                     // on each other's results
                     const int y = x - 16, sb = y & 1;
-                    sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[y >> 1], y < 2 ? mneg : sacc[sb], 0, 0, 0);
+                    sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[y >> 1], sacc[sb], 0, 0, 0);
                 }
                 if (x + RD < X1)
-                    buf[(x - X0) % RD] = rd(kso, vso, x + RD);
+                    buf[(x - X0) % RD] = rd(kb, vb, kso, vso, x + RD);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -461,8 +622,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         };
 
         // probabilities of the tile (f16 pairs, the PV operand) and their sum
-        auto probs = [&]() -> float {
-            float ls0 = 0.f, ls1 = 0.f;
+        // probabilities of the tile (f16 pairs, the PV operand)
+        auto probs = [&]() {
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
 #pragma unroll
@@ -470,18 +631,12 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                     const int r = 8 * (x & 1) + 2 * jj;
                     const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
                                         __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
-                    const half2v ph = __builtin_convertvector(pf, half2v);
-                    pw[x][jj] = __builtin_bit_cast(uint32_t, ph);
-                    if (jj & 1)
-                        ls1 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls1, false);
-                    else
-                        ls0 = __builtin_amdgcn_fdot2(ph, half2v{(_Float16)1.f, (_Float16)1.f}, ls0, false);
+                    pw[x][jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, half2v));
                 }
             }
-            return ls0 + ls1;
         };
-        // move the reference max up to the tile's row max (exact path)
-        auto move_max = [&](bool init) {
+        // row max of the tile's (masked) scores, over both lane halves
+        auto tile_max = [&]() -> float {
             float mx = -INFINITY;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
@@ -489,22 +644,21 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 for (int r = 0; r < 16; ++r)
                     mx = fmaxf(mx, sacc[sb][r]);
             }
-            mx = half_max(mx);
-            const float d = init ? mx : fmaxf(mx, 0.f);
-            if (!init) {
-                const float alpha = __builtin_amdgcn_exp2f(-d);
-                l_run *= alpha;
+            return half_max(mx);
+        };
+        // causal mask of tile j (only tiles reaching past the block's first query)
+        auto mask_tile = [&](int j) {
+            const int kb = j * KT;
+            if (kb + KT - 1 > hist + i0) {
+                const int lim = qlimit - kb - 4 * hh;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    o[db] *= alpha;
-            }
-            m_run += d;
-            mneg = floatx16(-m_run);
+                for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sacc[sb][r] -= d;
+                    for (int r = 0; r < 16; ++r) {
+                        if (32 * sb + 8 * (r >> 2) + (r & 3) > lim)
+                            sacc[sb][r] = -INFINITY;
+                    }
+                }
             }
         };
 
@@ -513,29 +667,17 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         auto phase_s = [&](auto stg_c, int j) {
             constexpr int STG = decltype(stg_c)::value;
             if (tile_active(j)) {
-                const int kb = j * KT;
-                // causal mask (only on tiles reaching past the block's first query)
-                if (kb + KT - 1 > hist + i0) {
-                    const int lim = qlimit - kb - 4 * hh;
-#pragma unroll
-                    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            if (32 * sb + 8 * (r >> 2) + (r & 3) > lim)
-                                sacc[sb][r] = -INFINITY;
-                        }
-                    }
-                }
+                mask_tile(j);
                 if (first) {
-                    move_max(true); // a row's first tile holds key 0, visible to every row
+                    // a row's first tile holds key 0, visible to every row
+                    const float mx = tile_max();
+                    m_run = mx;
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb)
+                        sacc[sb] -= mx;
                     first = false;
                 }
-                float lt = probs();
-                if (__builtin_amdgcn_ballot_w64(!(lt <= 3.0e38f))) {
-                    move_max(false);
-                    lt = probs();
-                }
-                l_run += lt;
+                probs();
             } else {
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
@@ -545,6 +687,18 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             prefetch(STG * TILE_B);
             wg_barrier();
         };
+
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            o[db] = floatx16{0.f};
+        lsum = floatx16{0.f};
+
+        // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        store_v<0>(vr, lds, vst);
+        if (ntiles > 1)
+            issue_v(vr, 1);
+        wg_barrier();
 
         if (grp == 1)
             wg_barrier(); // the trailing group starts one phase late
@@ -580,23 +734,36 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         if (grp == 0)
             wg_barrier(); // same barrier count for both groups
 
+        // An f16 probability past its range made a row sum infinite (or a NaN input made
+        // it NaN): the workgroup recomputes the unit on the exact path.  The flag holds the
+        // unit, so it never needs clearing.
+        if (__builtin_amdgcn_ballot_w64(!(lsum[0] <= 3.0e38f)) != 0 && lane == 0)
+            ovf_unit = v;
+        wg_barrier();
+        if (ovf_unit == v) {
+            exact_unit(p, lds, wdim, sdim, u, g, wk, hist);
+            continue;
+        }
+
         // ---- normalise and write.  The lane holds dims 32db + 8*(r/4) + 4*hh + r%4 of query
         // c; the rows pass through the wave's own 8 KB slice of LDS stages 2-3 (idle from the
         // last barrier until the next unit's first K tile 2 load, two barriers later), so
         // that every global store writes whole 256-byte rows instead of 8-byte pieces of 64
         // rows.  16-byte chunk k of row c sits at chunk k ^ (c % 16).
-        const float l_tot = half_sum(l_run);
-        const float inv = 1.f / l_tot;
+        const float inv = 1.f / lsum[0];
         char *ostage = lds + (wave < 4 ? 2 * TILE_B + wave * (QB * ROWB)
                                        : VREG_B + 2 * TILE_B + (wave - 4) * (QB * ROWB));
+        // chunk k of row c: the per-lane base with bits 4-7 flipped by k (opaque, so the
+        // sixteen addresses are not hoisted out of the unit loop into spilled registers)
+        uint32_t wbase = (uint32_t)((ostage - lds) + c * ROWB + ((c & 15) << 4) + hh * 8);
+        asm volatile("" : "+v"(wbase));
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
                 const u32x2 w = {pack2h(o[db][4 * ig + 0] * inv, o[db][4 * ig + 1] * inv),
                                  pack2h(o[db][4 * ig + 2] * inv, o[db][4 * ig + 3] * inv)};
-                const int chunk = (4 * db + ig) ^ (c & 15);
-                *reinterpret_cast<u32x2 *>(ostage + c * ROWB + chunk * 16 + hh * 8) = w;
+                *reinterpret_cast<u32x2 *>(lds + (wbase ^ (uint32_t)((4 * db + ig) << 4))) = w;
             }
         }
         // lanes read what other lanes wrote: keep the reads after the writes

@@ -83,8 +83,15 @@ def test_cache_append_bit_exact(kv):
 
 
 # ------------------------------------------------------------------ prefill / prefill_kv
-def run_prefill_kv(kv, cfg, lens, rope, poison=False, seed=None):
+def run_prefill_kv(kv, cfg, lens, rope, poison=False, seed=None, spike=None):
     inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32), poison_tail=poison, seed=seed)
+    if spike is not None:
+        # Dim 0 (left unrotated by a tail rotation) set to 1 in every q row and to 2048 in
+        # the new K row `spike` of every unit: rows that see that key score it some 250 log2
+        # units above anything else, far past the f16 (and fp32) range of 2^(score - max),
+        # while every other score keeps its size.  Both values are exact in f16.
+        inp.q[..., 0] = 1.0
+        inp.k[:, spike, :, 0] = 2048.0
     rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
     ref_out, ref64, k64 = oracle.prefill_kv(bits(inp.q), bits(inp.k), bits(inp.v),
                                             inp.positions.numpy(), rk, rv, inp.lens.numpy(),
@@ -144,6 +151,43 @@ def test_prefill_kv_shapes(kv, n, t, hq, hkv, lens, rope):
     cfg = custom(n, t, hq, hkv, max(lens) + t + 5, rope=rope, seed=300 + t)
     inp, d, out, ref = run_prefill_kv(kv, cfg, lens, rope)
     check_prefill(d, out, ref, lens, t, f"prefill_kv n{n} t{t} {hq}/{hkv} {lens}")
+
+
+def score_rise_log2(inp, ref, lens, rope, scale, hq, hkv):
+    """Largest rise, over all rows, of a visible score above the row's max over keys
+    0..63 (log2 units), from the oracle's rotated q and keys."""
+    k64, rk = ref[2], ref[3]
+    n, t = inp.q.shape[0], inp.q.shape[1]
+    _, q64 = oracle.rope(bits(inp.q).reshape(n * t, hq, -1), inp.positions.numpy().reshape(-1),
+                         ora_rope(rope))
+    q64 = q64.reshape(n, t, hq, -1)
+    g_size = hq // hkv
+    rise = -np.inf
+    for u in range(n):
+        L = int(lens[u])
+        for h in range(hq):
+            g = h // g_size
+            keys = np.concatenate([rk[u, g, :L].view(np.float16).astype(np.float64), k64[u][:, g, :]])
+            sc = q64[u, :, h, :] @ keys.T * scale * np.log2(np.e)          # [t, L + t]
+            for i in range(t):
+                vis = sc[i, :L + i + 1]
+                rise = max(rise, vis.max() - vis[:64].max())
+    return rise
+
+
+@pytest.mark.parametrize("n,t,hq,hkv,lens,spike", [
+    (2, 130, 12, 2, [0, 0], 100),      # prefill
+    (2, 45, 32, 2, [37, 100], 40),     # prefill_kv
+])
+def test_prefill_score_spike(kv, n, t, hq, hkv, lens, spike):
+    rope = W.YARN_TAIL_64
+    cfg = custom(n, t, hq, hkv, max(lens) + t + 5, rope=rope, seed=500 + t)
+    inp, d, out, ref = run_prefill_kv(kv, cfg, lens, rope, spike=spike)
+    # the spike does what it is meant to: some row's scores rise more than 16 (log2 units,
+    # with the kernel's scale) above the max over its first 64 keys, so 2^(score - max)
+    # leaves the f16 range and the kernel must fall back to its exact path
+    assert score_rise_log2(inp, ref, lens, rope, cfg.scale, hq, hkv) > 16.0
+    check_prefill(d, out, ref, lens, t, f"score-spike prefill n{n} t{t} {hq}/{hkv} {lens}")
 
 
 def test_prefill_poisoned_tail_is_never_read(kv):
