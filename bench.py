@@ -41,17 +41,17 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 269.142e6,
-        "src": ("329ffff231d871dde6badcf07219febf84acc7bbdb483bbfe1edad977d00ca5b",
-                "090b0feb4425e0e50f391526c9cf2d400cce8f7fc1080f177b2d1db555b5f0df")},
+        "bytes": 265.946e6,
+        "src": ("aafa3b615108c3eb3ea0c7dcc2f062d5f48404d6a19e97a121b8e10e1af543f2",
+                "16d1b200f8085a56e2d1747d4107f847c84ac804d3a328d0352dbb5dd12f2d35")},
     "decode_split:qwen1p5b_decode_l4096_b32": {
-        "bytes": 2.82754e9,
-        "src": ("598c87dd6c477fb2222df469535a04f0f3f817248b59182b139fe17e6a52a8dd",
-                "090b0feb4425e0e50f391526c9cf2d400cce8f7fc1080f177b2d1db555b5f0df")},
+        "bytes": 2.83169e9,
+        "src": ("0e827424de0e7e6905cc1a0a1f7ba89cbabc21d4a17de32473e8efcf9a8819aa",
+                "16d1b200f8085a56e2d1747d4107f847c84ac804d3a328d0352dbb5dd12f2d35")},
     "decode_split:yarn_decode_l32k_b64": {
-        "bytes": 23.0181e9,
-        "src": ("598c87dd6c477fb2222df469535a04f0f3f817248b59182b139fe17e6a52a8dd",
-                "090b0feb4425e0e50f391526c9cf2d400cce8f7fc1080f177b2d1db555b5f0df")},
+        "bytes": 23.03676e9,
+        "src": ("0e827424de0e7e6905cc1a0a1f7ba89cbabc21d4a17de32473e8efcf9a8819aa",
+                "16d1b200f8085a56e2d1747d4107f847c84ac804d3a328d0352dbb5dd12f2d35")},
 }
 KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_split": "decode.hip"}
 
