@@ -130,6 +130,7 @@ def bench_prefill(kv, W, name, steps, warmup):
 
 
 def bench_decode(kv, W, name, steps, warmup):
+    import numpy as np
     import torch
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg, device="cuda")
@@ -160,9 +161,45 @@ def bench_decode(kv, W, name, steps, warmup):
     call_ms = sum(ca[i].elapsed_time(cb[i]) for i in range(steps)) / steps
     k_ms = sum(evb[i].elapsed_time(eva[i]) for i in range(steps)) / steps
     nbytes = decode_bytes(lens, cfg.hq, cfg.hkv, cfg.d)
+    # measured ceiling of this access pattern: a kernel that only reads the same cache
+    # rows (rows 0..len of K and V, 1536-row chunks per workgroup, as the split kernel
+    # takes for these shapes), timed the same way
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    pa, pb = make_events(steps), make_events(steps)
+    for i in range(steps):
+        flush.fill_(i & 0xff)
+        pa[i].record()
+        kv.probe_stream(inp.cache_k, inp.cache_v, inp.lens, max_len, 1536, sink)
+        pb[i].record()
+    torch.cuda.synchronize()
+    probe_ms = sum(pa[i].elapsed_time(pb[i]) for i in range(steps)) / steps
+    probe_bytes = 2 * cfg.hkv * cfg.d * 2 * int((lens.astype(np.int64) + 1).sum())
     del inp, flush, ws
     torch.cuda.empty_cache()
-    return cfg, call_ms, k_ms, nbytes
+    return cfg, call_ms, k_ms, nbytes, probe_bytes / probe_ms / 1e6
+
+
+def measured_mfma(kv):
+    """f16 MFMA throughput a plain chain of independent 32x32x16 MFMAs reaches (two waves
+    per SIMD on every CU), and the shader clock the matrix cores ran at meanwhile."""
+    import torch
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * ncu, 4096
+    sink = torch.zeros(4 + 4 * blocks, dtype=torch.int64, device="cuda")
+    kv.probe_mfma(blocks, 64, sink)                 # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = make_events(2)
+    e0.record()
+    kv.probe_mfma(blocks, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = blocks * 4 * iters * 4 * (2 * 32 * 32 * 16)
+    c = sink[4:].view(blocks, 4).cpu().double()
+    mhz = float(((c[:, 3] - c[:, 2]) / (c[:, 1] - c[:, 0])).mean()) * 100.0
+    return {"mfma_f16_tflops": round(flops / ms / 1e9, 1), "sclk_mhz": round(mhz, 0),
+            "what": f"{blocks} workgroups x 4 waves x {iters} rounds of 4 independent "
+                    f"v_mfma_f32_32x32x16_f16; clock from the shader and 100 MHz counters"}
 
 
 def cpu_baseline(W, name, units):
@@ -235,19 +272,28 @@ def main():
     if not args.no_decode:
         for name in ["qwen1p5b_decode_l4096_b32", "yarn_decode_l32k_b64"]:
             log(f"[bench] decode {name}")
-            dcfg, call_ms, dk_ms, nbytes = bench_decode(kv, W, name, max(3, args.steps // 2),
-                                                        min(args.warmup, 3))
+            dcfg, call_ms, dk_ms, nbytes, ceil_gbs = bench_decode(kv, W, name, max(3, args.steps // 2),
+                                                                  min(args.warmup, 3))
             gbs = nbytes / (call_ms * 1e-3) / 1e9
             kgbs = nbytes / (dk_ms * 1e-3) / 1e9
             log(f"[bench] decode {name}: {call_ms * 1e3:.1f} us/step, split kernel "
-                f"{dk_ms * 1e3:.1f} us, {gbs:.0f} GB/s step, {kgbs:.0f} GB/s kernel")
+                f"{dk_ms * 1e3:.1f} us, {gbs:.0f} GB/s step, {kgbs:.0f} GB/s kernel; "
+                f"read-only stream of the same rows {ceil_gbs:.0f} GB/s")
             decode.append({"workload": name, "value": round(gbs, 1), "unit": "GB/s",
                            "ms_per_step": round(call_ms, 4), "bytes_per_step": nbytes,
                            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                            "roofline": {"bound": "hbm", "achieved": round(kgbs, 1),
                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                         "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                                        "traffic": traffic("decode_split", name)}})
+                                        "traffic": traffic("decode_split", name)},
+                           "stream_ceiling": {"value": round(ceil_gbs, 1), "unit": "GB/s",
+                                              "what": "read-only kernel over the same cache rows, "
+                                                      "same chunking",
+                                              "kernel_frac": round(kgbs / ceil_gbs, 4)}})
+
+    ceilings = measured_mfma(kv)
+    log(f"[bench] f16 MFMA microbenchmark: {ceilings['mfma_f16_tflops']:.0f} TFLOP/s at "
+        f"{ceilings['sclk_mhz']:.0f} MHz shader clock")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -275,6 +321,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": traffic("prefill_attn", cfg.name)},
         "decode": decode,
+        "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

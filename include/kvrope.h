@@ -166,6 +166,29 @@ int kvrope_set_profile_events(void *before, void *after);
  * value, compiled for the host: lets a CPU-only test check it on any input. */
 uint16_t kvrope_f64_to_f16(double x);
 
+/* ---- Measurement helpers (not part of the attention path): the measured ceilings a
+ * benchmark reports beside the spec peaks.
+ *
+ * kvrope_probe_stream -- reads, and only reads, the cache rows a decode step reads:
+ * rows [0, lens[u]] of K and V of every (unit, KV head) (cache_k, cache_v, lens laid out
+ * as for attn_decode), split into chunks of `chunk` rows (a multiple of 64) per
+ * workgroup like the decode kernel, 16-byte lane loads.  Its time is the streaming
+ * ceiling of that access pattern.  `sink` (device, >= 4 bytes) is never written in
+ * practice.  Requires max_len + 1 <= s_cap; a row past s_cap is never read.
+ *
+ * kvrope_probe_mfma -- `blocks` workgroups of 4 waves; each wave runs `iters` rounds of
+ * four independent v_mfma_f32_32x32x16_f16 chains (32 x 32 x 16 x 2 FLOPs each).
+ * sink (device, >= 32 * (blocks + 1) bytes): for workgroup b, sink[4 + 4b .. 4b + 7] as
+ * uint64 = real-time counter (100 MHz) at start and end, shader-clock counter at start
+ * and end; their ratio gives the clock the matrix cores ran at.
+ *
+ * Both return KVROPE_OK, KVROPE_ERR_NULL, KVROPE_ERR_SHAPE, KVROPE_ERR_CAPACITY (stream)
+ * or KVROPE_ERR_HIP, and are asynchronous on `stream`. */
+int kvrope_probe_stream(const void *cache_k, const void *cache_v, const int32_t *lens, int n,
+                        int hkv, int s_cap, int d, int max_len, int chunk, void *sink,
+                        void *stream);
+int kvrope_probe_mfma(int blocks, int iters, void *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

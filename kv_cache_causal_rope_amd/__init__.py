@@ -38,7 +38,8 @@ KVROPE_OP_DECODE = 1
 # every symbol include/kvrope.h declares
 EXPORTS = ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
            "attn_decode", "kvrope_workspace_size", "kvrope_status_string",
-           "kvrope_last_hip_error", "kvrope_set_profile_events", "kvrope_f64_to_f16"]
+           "kvrope_last_hip_error", "kvrope_set_profile_events", "kvrope_f64_to_f16",
+           "kvrope_probe_stream", "kvrope_probe_mfma"]
 
 
 class KVRopeError(RuntimeError):
@@ -114,8 +115,11 @@ def lib() -> ctypes.CDLL:
     L.kvrope_set_profile_events.argtypes = [_P, _P]
     L.kvrope_f64_to_f16.argtypes = [ctypes.c_double]
     L.kvrope_f64_to_f16.restype = ctypes.c_uint16
+    L.kvrope_probe_stream.argtypes = [_P, _P, _P] + [_I] * 6 + [_P, _P]
+    L.kvrope_probe_mfma.argtypes = [_I, _I, _P, _P]
     for rtn in ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
-                "attn_decode", "kvrope_set_profile_events"]:
+                "attn_decode", "kvrope_set_profile_events", "kvrope_probe_stream",
+                "kvrope_probe_mfma"]:
         getattr(L, rtn).restype = _I
     _lib = L
     return L
@@ -176,6 +180,23 @@ def set_profile_events(before: Optional[torch.cuda.Event], after: Optional[torch
 def f64_to_f16_bits(x: float) -> int:
     """The kernels' fp64 -> f16 conversion, run on the host (for tests)."""
     return int(lib().kvrope_f64_to_f16(float(x)))
+
+
+def probe_stream(cache_k, cache_v, lens, max_len: int, chunk: int, sink, stream=None):
+    """Read (only) rows [0, lens[u]] of every (unit, KV head) of the caches, in chunks of
+    `chunk` rows per workgroup: the streaming ceiling of a decode step's reads."""
+    n, hkv, s_cap, d = cache_k.shape
+    _f16("cache_k", cache_k, (n, hkv, s_cap, d))
+    _f16("cache_v", cache_v, (n, hkv, s_cap, d))
+    _i32("lens", lens, (n,))
+    _check(lib().kvrope_probe_stream(_ptr(cache_k), _ptr(cache_v), _ptr(lens), n, hkv, s_cap, d,
+                                     int(max_len), int(chunk), _ptr(sink), _stream(stream)))
+
+
+def probe_mfma(blocks: int, iters: int, sink, stream=None):
+    """`blocks` workgroups x 4 waves, each `iters` rounds of 4 independent f16 MFMAs
+    (32x32x16); sink (uint64) gets per-workgroup clock counters at [4 + 4b, 8 + 4b)."""
+    _check(lib().kvrope_probe_mfma(int(blocks), int(iters), _ptr(sink), _stream(stream)))
 
 
 def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope: RopeParams, stream=None):

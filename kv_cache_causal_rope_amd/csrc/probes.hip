@@ -1,0 +1,135 @@
+// probes.hip -- measured ceilings that the benchmark reports beside the spec peaks
+// (gfx950): a read-only stream over exactly the cache rows a decode step reads, with the
+// decode kernel's own (unit, KV head, key chunk) decomposition, and an f16 MFMA
+// microbenchmark that also records the shader clock it ran at.
+//
+// Both kernels compute nothing that is used: every lane folds what it read (or its
+// accumulators) into one word and writes it only when it equals a value no input
+// produces in practice, so the loads and MFMAs cannot be optimised away while the
+// writes cost nothing.
+#include "device_common.h"
+#include "kvrope.h"
+
+#include <stdint.h>
+
+namespace kvrope {
+
+namespace {
+
+constexpr uint32_t kNever = 0x7f3a91c5u;
+
+// One workgroup per (unit, KV head, chunk of `chunk` rows), 256 threads; rows
+// [0, lens[u]] of K and V (the cache rows of a decode step with the new row appended).
+// Each iteration reads 16 rows of K and 16 of V (4 KB each) as 16-byte lane loads, four
+// iterations in flight.
+__global__ void __launch_bounds__(256) stream_rows_kernel(const uint16_t *__restrict__ ck,
+                                                          const uint16_t *__restrict__ cv,
+                                                          const int32_t *__restrict__ lens, int hkv,
+                                                          int s_cap, int chunk, int nsplit,
+                                                          uint32_t *__restrict__ sink)
+{
+    int b = blockIdx.x;
+    const int split = b % nsplit;
+    b /= nsplit;
+    const int g = b % hkv, u = b / hkv;
+    const int nk = lens[u] + 1;
+    const int k0 = split * chunk;
+    if (k0 >= nk)
+        return;
+    const int k1 = min(min(k0 + chunk, nk), s_cap);
+    const size_t slab = ((size_t)u * hkv + g) * (size_t)s_cap * kHeadDim;
+    const u32x4 *K = reinterpret_cast<const u32x4 *>(ck + slab);
+    const u32x4 *V = reinterpret_cast<const u32x4 *>(cv + slab);
+    const int t = threadIdx.x;
+    uint32_t acc = 0;
+    for (int r0 = k0; r0 < k1; r0 += 64) {
+        u32x4 a[4], c[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int row = min(r0 + 16 * x + (t >> 4), k1 - 1);
+            a[x] = K[(size_t)row * 16 + (t & 15)];
+            c[x] = V[(size_t)row * 16 + (t & 15)];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            acc ^= a[x][0] ^ a[x][1] ^ a[x][2] ^ a[x][3] ^ c[x][0] ^ c[x][1] ^ c[x][2] ^ c[x][3];
+    }
+    if (acc == kNever)
+        sink[0] = acc;
+}
+
+// Every wave runs `iters` rounds of four independent v_mfma_f32_32x32x16_f16 chains.
+// Thread 0 of each workgroup records the 100 MHz real-time counter and the shader-clock
+// counter at its start and end (sink[4 + 4 b ...]).
+__global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, uint32_t seed, uint64_t *__restrict__ sink)
+{
+    uint64_t r0 = 0, m0 = 0;
+    if (threadIdx.x == 0)
+        asm volatile("s_memrealtime %0\n\ts_memtime %1\n\ts_waitcnt lgkmcnt(0)" : "=s"(r0), "=s"(m0));
+    const _Float16 x = (_Float16)((float)((seed + threadIdx.x) & 7) * 0.001f);
+    const half8 a = {x, x, x, x, x, x, x, x};
+    const half8 bop = {x, -x, x, -x, x, -x, x, -x};
+    floatx16 c0 = {0.f}, c1 = {0.f}, c2 = {0.f}, c3 = {0.f};
+    for (int i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bop, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop, a, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop, bop, c3, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        s += c0[r] + c1[r] + c2[r] + c3[r];
+    if (__builtin_bit_cast(uint32_t, s) == kNever)
+        sink[0] = 1;
+    if (threadIdx.x == 0) {
+        uint64_t r1, m1;
+        asm volatile("s_memrealtime %0\n\ts_memtime %1\n\ts_waitcnt lgkmcnt(0)" : "=s"(r1), "=s"(m1));
+        uint64_t *d = sink + 4 + 4 * (size_t)blockIdx.x;
+        d[0] = r0;
+        d[1] = r1;
+        d[2] = m0;
+        d[3] = m1;
+    }
+}
+
+} // namespace
+
+} // namespace kvrope
+
+extern "C" {
+
+int kvrope_probe_stream(const void *cache_k, const void *cache_v, const int32_t *lens, int n,
+                        int hkv, int s_cap, int d, int max_len, int chunk, void *sink, void *stream)
+{
+    if (!cache_k || !cache_v || !lens || !sink)
+        return KVROPE_ERR_NULL;
+    if (n < 0 || hkv < 1 || s_cap < 1 || d != kvrope::kHeadDim || chunk < 64 || chunk % 64 != 0)
+        return KVROPE_ERR_SHAPE;
+    if (max_len < 0 || max_len + 1 > s_cap)
+        return KVROPE_ERR_CAPACITY;
+    if (n == 0)
+        return KVROPE_OK;
+    const int nsplit = (max_len + 1 + chunk - 1) / chunk;
+    const int64_t blocks = (int64_t)n * hkv * nsplit;
+    if (blocks > 0x7fffffff)
+        return KVROPE_ERR_SHAPE;
+    hipLaunchKernelGGL(kvrope::stream_rows_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t *>(cache_k),
+                       static_cast<const uint16_t *>(cache_v), lens, hkv, s_cap, chunk, nsplit,
+                       static_cast<uint32_t *>(sink));
+    return hipGetLastError() == hipSuccess ? KVROPE_OK : KVROPE_ERR_HIP;
+}
+
+int kvrope_probe_mfma(int blocks, int iters, void *sink, void *stream)
+{
+    if (!sink)
+        return KVROPE_ERR_NULL;
+    if (blocks < 1 || iters < 1)
+        return KVROPE_ERR_SHAPE;
+    hipLaunchKernelGGL(kvrope::mfma_probe_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), iters, 12345u, static_cast<uint64_t *>(sink));
+    return hipGetLastError() == hipSuccess ? KVROPE_OK : KVROPE_ERR_HIP;
+}
+
+} // extern "C"

@@ -309,3 +309,21 @@ def test_out_of_range_length_yields_nan_and_no_write(kv):
     torch.cuda.synchronize()
     assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
     assert torch.equal(d.cache_k[1], ck0[1])
+
+
+def test_measurement_probes_run(kv):
+    """The ceiling probes bench.py reports: the stream probe reads a small cache without
+    error, and the MFMA probe records a shader clock between 0.5 and 3 GHz."""
+    cfg = custom(3, 1, 12, 2, 300, seed=900)
+    inp = W.make_inputs(cfg, lens=np.array([0, 150, 299], np.int32))
+    d = to_dev(inp)
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    kv.probe_stream(d.cache_k, d.cache_v, d.lens, 299, 128, sink)
+    blocks = 8
+    clk = torch.zeros(4 + 4 * blocks, dtype=torch.int64, device="cuda")
+    kv.probe_mfma(blocks, 256, clk)
+    torch.cuda.synchronize()
+    c = clk[4:].view(blocks, 4).cpu().double()
+    assert bool((c[:, 1] > c[:, 0]).all()) and bool((c[:, 3] > c[:, 2]).all())
+    mhz = float(((c[:, 3] - c[:, 2]) / (c[:, 1] - c[:, 0])).mean()) * 100.0
+    assert 500.0 < mhz < 3000.0, mhz
