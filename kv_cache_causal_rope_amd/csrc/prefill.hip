@@ -103,6 +103,16 @@ struct PrefillParams {
 // with vmcnt; the memory clobber keeps the compiler from moving memory ops across it.
 __device__ inline void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The barrier that ends a softmax phase: its LDS stores must be complete, but the RD
+// operand reads it issued last (for the next MFMA phase) may stay in flight.  LDS
+// operations of a wave complete in order, so at most RD outstanding means every store
+// (issued before the reads) is done.
+template <int N>
+__device__ inline void wg_barrier_reads_in_flight()
+{
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" : : "i"(N) : "memory");
+}
+
 __device__ inline int kswz(int key) { return key & 15; }
 
 __device__ inline uint32_t lds_offset(const void *p)
@@ -685,7 +695,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
             stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
             prefetch(STG * TILE_B);
-            wg_barrier();
+            wg_barrier_reads_in_flight<RD>();
         };
 
 #pragma unroll
