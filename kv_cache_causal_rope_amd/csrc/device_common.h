@@ -78,6 +78,26 @@ __host__ __device__ inline uint16_t f64_to_f16_rne(double x)
     return (uint16_t)(sign | (uint16_t)qv);
 }
 
+// fp64 -> IEEE binary16, round to nearest even, on the conversion units: x is rounded to
+// f32 by rounding to odd (the nearest f32, stepped back toward zero when it rounded
+// away, with its last bit set when inexact), then f32 -> f16 rounds to nearest even.
+// Rounding to odd at 24 bits keeps the second rounding to 11 bits exact, so the result
+// equals f64_to_f16_rne bit for bit (NaN: the same quiet NaN).
+__device__ inline uint16_t f64_to_f16_rne_dev(double x)
+{
+    if (x != x)
+        return (uint16_t)((__builtin_bit_cast(uint64_t, x) >> 48) & 0x8000u) | 0x7e00u;
+    const float f = (float)x;
+    const double back = (double)f;
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    if (back != x) {
+        if (__builtin_fabs(back) > __builtin_fabs(x))
+            b -= 1u;
+        b |= 1u;
+    }
+    return __builtin_bit_cast(uint16_t, (_Float16)__builtin_bit_cast(float, b));
+}
+
 __device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 // Low / high f16 of a 32-bit word, widened to fp32.

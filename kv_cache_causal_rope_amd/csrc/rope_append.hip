@@ -5,7 +5,10 @@
 // c = cos(theta) * mscale, s = sin(theta) * mscale the pair (x0, x1) becomes
 // (x0 c - x1 s, x0 s + x1 c).  These kernels evaluate it in fp64 and round once to f16
 // (nearest even), so a rotated K row in the cache is the correctly rounded f16 of the
-// exact rotation.
+// exact rotation.  The angle is taken in turns (pos * w[j] / 2 pi, reduced exactly to a
+// fraction of a turn) and its sine and cosine come from Taylor series on at most an
+// eighth of a turn: within a few 1e-16 of fp64 sin / cos of pos * w[j], at a fraction
+// of their cost.
 //
 // Append (Sophgo MLIR-based LLM compilation paper, sec. 3.1 Listing 2: Concat(history,
 // new); Buddy-MLIR walkthrough, sec. 6.4.5): new row i of unit u goes to cache row
@@ -33,12 +36,37 @@ __device__ inline void rotate_chunk_f64(const uint16_t (&in)[8], uint16_t (&out)
             const double x1 = h2d(in[2 * m + 1]);
             const double y0 = x0 * cs[m] - x1 * sn[m];
             const double y1 = x0 * sn[m] + x1 * cs[m];
-            out[2 * m] = f64_to_f16_rne(y0);
-            out[2 * m + 1] = f64_to_f16_rne(y1);
+            out[2 * m] = f64_to_f16_rne_dev(y0);
+            out[2 * m + 1] = f64_to_f16_rne_dev(y1);
         } else {
             out[2 * m] = in[2 * m];
             out[2 * m + 1] = in[2 * m + 1];
         }
+    }
+}
+
+// sin(2 pi r) and cos(2 pi r) in fp64.  r - rint(r) = f in [-1/2, 1/2] is exact; so is
+// g = f - q/4 with q = rint(4 f) the nearest quarter turn, |g| <= 1/8.  For x = 2 pi g
+// (|x| <= pi/4) the Taylor series of sin through x^15 and of cos through x^16 leave a
+// remainder below 5e-17; the quarter turns q then rotate (sin x, cos x).
+__device__ inline void sincos_turns(double r, double &s, double &c)
+{
+    const double f = r - __builtin_rint(r);
+    const double q = __builtin_rint(4.0 * f);
+    const double x = (f - 0.25 * q) * 6.283185307179586476925;
+    const double x2 = x * x;
+    const double sx =
+        x * (1.0 + x2 * (-1.0 / 6 + x2 * (1.0 / 120 + x2 * (-1.0 / 5040 + x2 * (1.0 / 362880 +
+        x2 * (-1.0 / 39916800 + x2 * (1.0 / 6227020800.0 + x2 * (-1.0 / 1307674368000.0))))))));
+    const double cx =
+        1.0 + x2 * (-1.0 / 2 + x2 * (1.0 / 24 + x2 * (-1.0 / 720 + x2 * (1.0 / 40320 +
+        x2 * (-1.0 / 3628800 + x2 * (1.0 / 479001600.0 + x2 * (-1.0 / 87178291200.0 +
+        x2 * (1.0 / 20922789888000.0))))))));
+    switch ((int)q & 3) {
+    case 0: s = sx; c = cx; break;
+    case 1: s = cx; c = -sx; break;
+    case 2: s = -sx; c = -cx; break;
+    default: s = -cx; c = sx; break;
     }
 }
 
@@ -53,9 +81,8 @@ __device__ inline void chunk_trig(int c, double pos, const RopeTable &tab, doubl
         sn[m] = 0.0;
         if (dim >= tab.off) {
             const int j = (dim - tab.off) >> 1;
-            const double theta = pos * tab.w[j];
             double s, co;
-            sincos(theta, &s, &co);
+            sincos_turns(pos * tab.wrev[j], s, co);
             cs[m] = co * tab.mscale;
             sn[m] = s * tab.mscale;
         }
