@@ -239,6 +239,61 @@ __device__ inline void rotate_q(half8 (&qop)[8], const u32x4 (&qin)[8], int qpos
     }
 }
 
+// The rotation factors of a workgroup's tokens, shared by the query heads of a group:
+// entry (token k, dim pairs 4 g .. 4 g + 3) holds {cos, sin} of each pair, times the
+// pair's output scale, 32 bytes at byte (g * ntok + k) * 32 (a row of consecutive
+// tokens per pair group, so the lanes of a wave read consecutive entries).
+constexpr int TAB_B = 2 * TILE_B; // LDS byte offset: the K regions of stages 2 and 3
+
+// Fill the table for ntok tokens (32 or 64): thread tid computes token k = tid % ntok at
+// position tpos (that token's), pair groups (tid / ntok) * (ntok / 32) + 0 .. ntok / 32 - 1.
+// The factors are the ones rotate_q computes.
+__device__ inline void fill_rot_table(char *lds, int tpos, int ntok, int tid, const double *wdim,
+                                      const float *sdim)
+{
+    const int k = tid % ntok;
+    const int per = ntok / QB;
+    const double posd = (double)tpos;
+    for (int e = 0; e < per; ++e) {
+        const int g = (tid / ntok) * per + e;
+        floatx4 f[2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int dp = 4 * g + m;
+            const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp]);
+            const float sc = sdim[dp];
+            f[m >> 1][2 * (m & 1)] = __builtin_amdgcn_cosf(rf) * sc;
+            f[m >> 1][2 * (m & 1) + 1] = __builtin_amdgcn_sinf(rf) * sc;
+        }
+        floatx4 *dst = reinterpret_cast<floatx4 *>(lds + TAB_B + (g * ntok + k) * 32);
+        dst[0] = f[0];
+        dst[1] = f[1];
+    }
+}
+
+// rotate_q with the factors of table token k: dims 16 s + 8 hh + 2 m + {0, 1} are pair
+// 4 (2 s + hh) + m.
+__device__ inline void rotate_q_tab(half8 (&qop)[8], const u32x4 (&qin)[8], const char *lds, int ntok, int k,
+                                    int hh)
+{
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const floatx4 *src = reinterpret_cast<const floatx4 *>(lds + TAB_B + ((2 * s + hh) * ntok + k) * 32);
+        const floatx4 f0 = src[0], f1 = src[1];
+        const float cs[4] = {f0[0], f0[2], f1[0], f1[2]};
+        const float sn[4] = {f0[1], f0[3], f1[1], f1[3]};
+        const u32x4 in = qin[s];
+        u32x4 hv;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
+            const floatx2 y = {x0 * cs[m] - x1 * sn[m], x0 * sn[m] + x1 * cs[m]};
+            hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
+        }
+        qop[s] = __builtin_bit_cast(half8, hv);
+    }
+}
+
 // Rare path.  The fast path keeps each row's reference max from its first tile; when a
 // later key scores 2^16 or more above it, an f16 probability overflows and the row sum
 // turns infinite.  Then the whole workgroup recomputes the unit here with the running
@@ -490,6 +545,11 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const int iq = min(i, p.t - 1);
         const uint16_t *qrow = p.q + (((int64_t)u * p.t + iq) * p.hq + h) * kHeadDim;
         const int qpos = p.pos[(int64_t)u * p.t + iq];
+        // position of this thread's token of the unit's rotation table (see below; rows
+        // past t take row t - 1's), loaded first so that it arrives first
+        const int tb_first = (wk * NW) / p.G;
+        const int ntok = (tb_last - tb_first + 1) * QB;
+        const int tpos = p.pos[(int64_t)u * p.t + min(tb_first * QB + tid % ntok, p.t - 1)];
         u32x4 qin[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
@@ -500,9 +560,18 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         VRegs vr;
         issue_v(vr, 0);
 
-        // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16
+        // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16.
+        // When the unit's items span at most two token blocks, the workgroup computes each
+        // (token, pair) factor once into LDS instead of once per query head.
         half8 qop[8];
-        rotate_q(qop, qin, qpos, hh, wdim, sdim);
+        if (ntok <= 2 * QB) {
+            wg_barrier(); // every wave has read its previous unit's output rows back
+            fill_rot_table(lds, tpos, ntok, tid, wdim, sdim);
+            wg_barrier();
+            rotate_q_tab(qop, qin, lds, ntok, (tb - tb_first) * QB + c, hh);
+        } else {
+            rotate_q(qop, qin, qpos, hh, wdim, sdim);
+        }
 
         // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
         // K operand of head-dim step s: chunk (2s + hh) ^ (c % 16) of key row c.  The step
