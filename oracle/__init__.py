@@ -28,7 +28,7 @@ from . import build as _build
 _lib = None
 
 
-@dataclasses.dataclass(frozen=True)
+@dataclasses.dataclass(frozen=True, eq=False)
 class RopeParams:
     base: float = 10000.0
     n_rot: int = 128
@@ -39,6 +39,13 @@ class RopeParams:
     beta_fast: float = 32.0
     beta_slow: float = 1.0
     mscale: float = 1.0
+    half_split: bool = False       # pairs (o + j, o + j + n_rot/2) instead of (o + 2j, o + 2j + 1)
+    inverse: bool = False          # rotate by -theta
+    cos_table: np.ndarray | None = None  # float32 [rows, n_rot/2], gathered by position
+    sin_table: np.ndarray | None = None
+
+    def replace(self, **kw) -> "RopeParams":
+        return dataclasses.replace(self, **kw)
 
     @staticmethod
     def plain(n_rot: int = 128, base: float = 10000.0) -> "RopeParams":
@@ -57,12 +64,31 @@ class _CRope(ctypes.Structure):
     _fields_ = [("base", ctypes.c_double), ("n_rot", ctypes.c_int32), ("yarn", ctypes.c_int32),
                 ("freq_scale", ctypes.c_double), ("ext_factor", ctypes.c_double),
                 ("n_ctx_orig", ctypes.c_int32), ("beta_fast", ctypes.c_double),
-                ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double)]
+                ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double),
+                ("pairing", ctypes.c_int32), ("inverse", ctypes.c_int32),
+                ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                ("table_rows", ctypes.c_int32)]
+
+
+def _table(a, half: int) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    assert a.ndim == 2 and a.shape[1] == half, a.shape
+    return a
 
 
 def _c_rope(rp: RopeParams) -> _CRope:
-    return _CRope(rp.base, rp.n_rot, int(rp.yarn), rp.freq_scale, rp.ext_factor,
-                  rp.n_ctx_orig, rp.beta_fast, rp.beta_slow, rp.mscale)
+    """The C parameter block.  It points into rp's tables: keep rp alive while it is used."""
+    c = _CRope(rp.base, rp.n_rot, int(rp.yarn), rp.freq_scale, rp.ext_factor,
+               rp.n_ctx_orig, rp.beta_fast, rp.beta_slow, rp.mscale, int(rp.half_split),
+               int(rp.inverse), None, None, 0)
+    if (rp.cos_table is None) != (rp.sin_table is None):
+        raise ValueError("cos_table and sin_table go together")
+    if rp.cos_table is not None:
+        ct, st = _table(rp.cos_table, rp.n_rot // 2), _table(rp.sin_table, rp.n_rot // 2)
+        assert ct.shape == st.shape
+        c.cos_table, c.sin_table, c.table_rows = ct.ctypes.data, st.ctypes.data, ct.shape[0]
+        c._keep = (ct, st)
+    return c
 
 
 _P = ctypes.c_void_p

@@ -118,6 +118,12 @@ typedef struct ora_rope_params {
     double beta_fast;   /* YaRN: correction-dim boundary (fast) */
     double beta_slow;   /* YaRN: correction-dim boundary (slow) */
     double mscale;      /* magnitude factor applied to both outputs of every rotated pair */
+    int32_t pairing;    /* 0: adjacent pairs (o + 2j, o + 2j + 1); 1: half-split pairs
+                           (o + j, o + j + n_rot/2) */
+    int32_t inverse;    /* 1: rotate by -theta (the sine's sign flipped) */
+    const float *cos_table; /* optional [table_rows][n_rot/2] factors gathered by position */
+    const float *sin_table; /* (both or neither); they replace cos/sin(theta) * mscale */
+    int32_t table_rows;
 } ora_rope_params;
 
 /* [ds4] Trace 1: the dimension index at which a pair turns `beta` full circles over the
@@ -179,23 +185,35 @@ void ora_rope_freqs(const ora_rope_params *rp, double *omega_eff, double *gamma_
 
 /* Rotate rows of x in place of a copy.
  * x, out: f16 [rows, h, d] (row-major, d innermost); positions: [rows].
- * [ds4] Trace 2 rotation of pair (x0, x1) = (x[o + 2j], x[o + 2j + 1]) with o = d - n_rot:
- *     c = cos(theta) * mscale,  s = sin(theta) * mscale,
+ * [ds4] Trace 2 rotation of pair j of a head, (x0, x1), o = d - n_rot:
+ *     c = cos(theta) * mscale,  s = sin_sign * sin(theta) * mscale,
  *     x0' = x0 * c - x1 * s,    x1' = x0 * s + x1 * c
- * i.e. the matrix [[cos, -sin], [sin, cos]] applied to adjacent pairs.
+ * i.e. the matrix [[cos, -sin], [sin, cos]] applied to the pair.
  * Reading: the rotated dims are the last n_rot dims of each head (the page's pointer to
  * the head start contradicts its own "tail" wording and the tail-rotation workload).
+ * Pairs: (x[o + 2j], x[o + 2j + 1]) as printed on the page (pairing 0), or
+ * (x[o + j], x[o + j + n_rot/2]) (pairing 1, the half-split convention of many
+ * checkpoints; the same rotation on a permuted pairing).
+ * sin_sign: [ds4] Trace 2 passes an `inverse` flag and multiplies sin by sin_sign; the
+ * excerpt omits its definition.  Reading: sin_sign = -1 when inverse, else +1.
+ * Tables: [Sophgo] Listings 1-2 gather precomputed cos / sin by position_ids
+ * (top.Gather(rotary_cos_w, pos_ids)) and hand them to top.Rope.  Reading: one value per
+ * rotated pair, rows indexed by position; the gathered values are the whole factor (no
+ * mscale); sin_sign still applies.  A position outside [0, table_rows) makes that row's
+ * rotated dims NaN.
  * Dims [0, o) are copied bit for bit.  out64 (optional) gets the unrounded fp64 values. */
 void ora_rope(const uint16_t *x, const int32_t *positions, int64_t rows, int h, int d,
               const ora_rope_params *rp, uint16_t *out, double *out64)
 {
     const int half = rp->n_rot / 2;
     const int o = d - rp->n_rot;
+    const double sin_sign = rp->inverse ? -1.0 : 1.0;
     double *omega = (double *)malloc(sizeof(double) * (size_t)(half > 0 ? half : 1));
     ora_rope_freqs(rp, omega, NULL, NULL);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const double pos = (double)positions[r];
+        const int in_table = rp->cos_table && positions[r] >= 0 && positions[r] < rp->table_rows;
         for (int hh = 0; hh < h; ++hh) {
             const int64_t base_idx = (r * h + hh) * (int64_t)d;
             for (int i = 0; i < o; ++i) {
@@ -204,19 +222,26 @@ void ora_rope(const uint16_t *x, const int32_t *positions, int64_t rows, int h, 
                     out64[base_idx + i] = ora_f16_to_f64(x[base_idx + i]);
             }
             for (int j = 0; j < half; ++j) {
-                const double theta = pos * omega[j];
-                const double c = cos(theta) * rp->mscale;
-                const double s = sin(theta) * rp->mscale;
-                const int64_t i0 = base_idx + o + 2 * j;
+                double c, s;
+                if (rp->cos_table) {
+                    c = in_table ? (double)rp->cos_table[(int64_t)positions[r] * half + j] : NAN;
+                    s = in_table ? sin_sign * (double)rp->sin_table[(int64_t)positions[r] * half + j] : NAN;
+                } else {
+                    const double theta = pos * omega[j];
+                    c = cos(theta) * rp->mscale;
+                    s = sin_sign * sin(theta) * rp->mscale;
+                }
+                const int64_t i0 = base_idx + o + (rp->pairing ? j : 2 * j);
+                const int64_t i1 = i0 + (rp->pairing ? half : 1);
                 const double x0 = ora_f16_to_f64(x[i0]);
-                const double x1 = ora_f16_to_f64(x[i0 + 1]);
+                const double x1 = ora_f16_to_f64(x[i1]);
                 const double y0 = x0 * c - x1 * s;
                 const double y1 = x0 * s + x1 * c;
                 out[i0] = ora_f64_to_f16(y0);
-                out[i0 + 1] = ora_f64_to_f16(y1);
+                out[i1] = ora_f64_to_f16(y1);
                 if (out64) {
                     out64[i0] = y0;
-                    out64[i0 + 1] = y1;
+                    out64[i1] = y1;
                 }
             }
         }

@@ -33,8 +33,23 @@ MUTANTS = [
     ("YaRN mix swapped", "w = omega * (rp->freq_scale * (1.0 - gamma) + gamma);",
      "w = omega * (rp->freq_scale * gamma + (1.0 - gamma));",
      [R.test_yarn_limits_equal_plain_rotation]),
-    ("mscale dropped", "const double c = cos(theta) * rp->mscale;", "const double c = cos(theta);",
+    ("mscale dropped", "c = cos(theta) * rp->mscale;", "c = cos(theta);",
      [R.test_pair_norm_scaled_by_mscale_only, R.test_yarn_position_zero_scales_by_mscale]),
+    ("half-split partner adjacent", "const int64_t i1 = i0 + (rp->pairing ? half : 1);",
+     "const int64_t i1 = i0 + (rp->pairing ? 1 : 1);",
+     [R.test_half_split_is_adjacent_rotation_of_permuted_dims,
+      R.test_half_split_matches_complex_multiplication]),
+    ("half-split pairs from the head start", "const int64_t i0 = base_idx + o + (rp->pairing ? j : 2 * j);",
+     "const int64_t i0 = base_idx + (rp->pairing ? j : o + 2 * j);",
+     [R.test_half_split_tail_keeps_head_dims]),
+    ("inverse ignored", "const double sin_sign = rp->inverse ? -1.0 : 1.0;", "const double sin_sign = 1.0;",
+     [R.test_inverse_at_pos_is_forward_at_minus_pos, R.test_inverse_undoes_forward_in_fp64]),
+    ("table column shifted", "(double)rp->cos_table[(int64_t)positions[r] * half + j]",
+     "(double)rp->cos_table[(int64_t)positions[r] * half + (j + 1) % half]",
+     [R.test_table_rotation_closed_form]),
+    ("table rows not by position", "(double)rp->sin_table[(int64_t)positions[r] * half + j]",
+     "(double)rp->sin_table[(int64_t)r % rp->table_rows * half + j]",
+     [R.test_table_gather_follows_positions, R.test_table_rotation_closed_form]),
     ("corr dim without 2", "(2.0 * M_PI * beta)", "(M_PI * beta)",
      [R.test_yarn_correction_dims_turn_beta_circles]),
     ("ramp inverted", "    return 1.0 - y;", "    return y;",

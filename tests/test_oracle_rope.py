@@ -208,3 +208,146 @@ def test_yarn_position_zero_scales_by_mscale(ora):
     xd = ora.f16_to_f64(x)
     np.testing.assert_allclose(y[..., 64:], xd[..., 64:] * rp.mscale, rtol=1e-15)
     assert np.array_equal(y[..., :64], xd[..., :64])
+
+
+# ---------------------------------------------------------------- rotation variants
+# Half-split pairing (pair j = dims (o + j, o + j + n_rot/2)), the inverse rotation
+# (ds4 Trace 2's `inverse` flag: the sine's sign flipped) and caller tables of cos / sin
+# gathered by position (Sophgo Listings 1-2: top.Gather(rotary_cos_w, pos_ids)).
+
+def _interleave(x, n_rot):
+    """Dims o + j and o + j + n_rot/2 of x placed at o + 2j and o + 2j + 1."""
+    d = x.shape[-1]
+    o, half = d - n_rot, n_rot // 2
+    y = x.copy()
+    y[..., o + 0:d:2] = x[..., o:o + half]
+    y[..., o + 1:d:2] = x[..., o + half:d]
+    return y
+
+
+@pytest.mark.parametrize("rp_name", ["plain", "yarn"])
+def test_half_split_is_adjacent_rotation_of_permuted_dims(ora, rp_name):
+    # The same rotation on a permuted pairing: interleaving the two halves, rotating with
+    # adjacent pairs and de-interleaving gives the half-split result bit for bit.
+    rp = ora.RopeParams.plain() if rp_name == "plain" else ora.RopeParams.yarn_tail()
+    rng = np.random.default_rng(21)
+    x = _rand_f16(rng, (9, 2, 128))
+    pos = rng.integers(0, 30000, 9).astype(np.int32)
+    hs, hs64 = ora.rope(x, pos, rp.replace(half_split=True))
+    adj, adj64 = ora.rope(_interleave(x, rp.n_rot), pos, rp)
+    assert np.array_equal(_interleave(hs, rp.n_rot), adj)
+    assert np.array_equal(_interleave(hs64, rp.n_rot), adj64)
+    # and it is a different pairing (dims really move between pairs)
+    assert not np.array_equal(hs, ora.rope(x, pos, rp)[0])
+
+
+def test_half_split_matches_complex_multiplication(ora):
+    # independent route: (x[j] + i x[j + 64]) * exp(i pos base^(-2j/128)) in complex128
+    rng = np.random.default_rng(22)
+    rows = 24
+    x = _rand_f16(rng, (rows, 2, 128))
+    pos = rng.integers(0, 5000, rows).astype(np.int32)
+    _, y = ora.rope(x, pos, ora.RopeParams.plain().replace(half_split=True))
+    xd = x.view(np.float16).astype(np.float64)
+    z = xd[..., :64] + 1j * xd[..., 64:]
+    freqs = np.power(10000.0, -np.arange(64) / 64.0)
+    w = z * np.exp(1j * pos[:, None, None] * freqs[None, None, :])
+    np.testing.assert_allclose(y[..., :64], w.real, atol=1e-11)
+    np.testing.assert_allclose(y[..., 64:], w.imag, atol=1e-11)
+
+
+def test_half_split_tail_keeps_head_dims(ora):
+    rp = ora.RopeParams.yarn_tail().replace(half_split=True)
+    rng = np.random.default_rng(23)
+    x = _rand_f16(rng, (6, 4, 128))
+    out, _ = ora.rope(x, rng.integers(1, 9000, 6).astype(np.int32), rp)
+    assert np.array_equal(out[..., :64], x[..., :64])
+    assert not np.array_equal(out[..., 64:], x[..., 64:])
+
+
+@pytest.mark.parametrize("rp_name", ["plain", "yarn", "half"])
+def test_inverse_at_pos_is_forward_at_minus_pos(ora, rp_name):
+    # R(-theta) = R(theta)^T: the inverse at p equals the forward rotation at -p, bit for
+    # bit (cos is even and sin odd, exactly, in fp64).
+    rp = {"plain": ora.RopeParams.plain(), "yarn": ora.RopeParams.yarn_tail(),
+          "half": ora.RopeParams.plain().replace(half_split=True)}[rp_name]
+    rng = np.random.default_rng(24)
+    x = _rand_f16(rng, (11, 2, 128))
+    pos = rng.integers(0, 20000, 11).astype(np.int32)
+    inv, inv64 = ora.rope(x, pos, rp.replace(inverse=True))
+    fwd, fwd64 = ora.rope(x, -pos, rp)
+    assert np.array_equal(inv, fwd)
+    assert np.array_equal(inv64, fwd64)
+
+
+def test_inverse_undoes_forward_in_fp64(ora):
+    # closed form: the inverse rotation of the exact forward rotation returns x; checked
+    # in complex128 as z * exp(i t) * exp(-i t) with the oracle supplying both halves
+    rng = np.random.default_rng(25)
+    x = _rand_f16(rng, (8, 1, 128))
+    pos = rng.integers(0, 4000, 8).astype(np.int32)
+    _, y = ora.rope(x, pos, ora.RopeParams.plain().replace(inverse=True))
+    xd = x.view(np.float16).astype(np.float64)
+    z = xd[..., 0::2] + 1j * xd[..., 1::2]
+    freqs = np.power(10000.0, -np.arange(64) / 64.0)
+    w = z * np.exp(-1j * pos[:, None, None] * freqs[None, None, :])
+    np.testing.assert_allclose(y[..., 0::2], w.real, atol=1e-11)
+    np.testing.assert_allclose(y[..., 1::2], w.imag, atol=1e-11)
+
+
+def _tables(rows, n_rot, base=10000.0):
+    j = np.arange(n_rot // 2)
+    ang = np.arange(rows)[:, None] * np.power(base, -2.0 * j / n_rot)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@pytest.mark.parametrize("half_split", [False, True])
+def test_table_rotation_closed_form(ora, half_split):
+    # with tables, each pair turns by the gathered (cos, sin): checked in complex128
+    # against the float32 table values themselves
+    rng = np.random.default_rng(26)
+    ct, st = _tables(3000, 128)
+    x = _rand_f16(rng, (10, 3, 128))
+    pos = rng.integers(0, 3000, 10).astype(np.int32)
+    rp = ora.RopeParams.plain().replace(cos_table=ct, sin_table=st, half_split=half_split)
+    _, y = ora.rope(x, pos, rp)
+    xd = x.view(np.float16).astype(np.float64)
+    a, b = (xd[..., :64], xd[..., 64:]) if half_split else (xd[..., 0::2], xd[..., 1::2])
+    rot = ct[pos].astype(np.float64)[:, None, :] + 1j * st[pos].astype(np.float64)[:, None, :]
+    w = (a + 1j * b) * rot
+    ya, yb = (y[..., :64], y[..., 64:]) if half_split else (y[..., 0::2], y[..., 1::2])
+    np.testing.assert_allclose(ya, w.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(yb, w.imag, rtol=0, atol=1e-12)
+
+
+def test_table_gather_follows_positions(ora):
+    # identity rows rotate nothing; permuting the table rows together with the positions
+    # changes nothing; a position past the table makes the rotated dims NaN
+    rng = np.random.default_rng(27)
+    ct, st = _tables(64, 64)
+    x = _rand_f16(rng, (6, 2, 128))
+    pos = np.array([0, 5, 63, 17, 40, 2], np.int32)
+    rp = ora.RopeParams.yarn_tail().replace(cos_table=ct, sin_table=st)
+    out, _ = ora.rope(x, pos, rp)
+    perm = rng.permutation(64)
+    inv = np.argsort(perm)
+    out_p, _ = ora.rope(x, inv[pos].astype(np.int32), rp.replace(cos_table=ct[perm], sin_table=st[perm]))
+    assert np.array_equal(out, out_p)
+    one, zero = np.ones_like(ct), np.zeros_like(st)
+    ident, _ = ora.rope(x, pos, rp.replace(cos_table=one, sin_table=zero))
+    assert np.array_equal(ident, x)
+    bad, bad64 = ora.rope(x, np.array([0, 64, -1, 3, 3, 3], np.int32), rp)
+    assert np.isnan(bad64[1:3, :, 64:]).all() and not np.isnan(bad64[[0, 3], :, 64:]).any()
+    assert np.array_equal(bad[1:3, :, :64], x[1:3, :, :64])
+
+
+def test_table_of_the_schedule_matches_computed_rotation(ora):
+    # tables holding fp32-rounded cos / sin of the plain schedule agree with the computed
+    # rotation to fp32 accuracy of the factors
+    rng = np.random.default_rng(28)
+    ct, st = _tables(5000, 128)
+    x = _rand_f16(rng, (12, 2, 128))
+    pos = rng.integers(0, 5000, 12).astype(np.int32)
+    _, yt = ora.rope(x, pos, ora.RopeParams.plain().replace(cos_table=ct, sin_table=st))
+    _, yc = ora.rope(x, pos, ora.RopeParams.plain())
+    np.testing.assert_allclose(yt, yc, rtol=0, atol=5e-7 * np.abs(x.view(np.float16)).max() * 2)
