@@ -65,16 +65,25 @@ extern "C" {
 #define KVROPE_ERR_HIP (-8)       /* a HIP launch failed (see kvrope_last_hip_error) */
 
 /* Rotary embedding parameters ([ds4] Traces 1-2).
- * Pair j = 0 .. n_rot/2-1 of a head rotates dims (d - n_rot + 2j, d - n_rot + 2j + 1)
- * by theta = pos * w_j with
+ * Pair j = 0 .. n_rot/2-1 of a head, with o = d - n_rot, is the dims
+ *     (o + 2j, o + 2j + 1)          pairing 0 (adjacent, as the trace prints it)
+ *     (o + j, o + j + n_rot/2)      pairing 1 (half-split; requires n_rot % 32 == 0)
+ * and turns by theta = pos * w_j with
  *     w_j = base^(-2j / n_rot)                                   (plain)
  *     w_j = base^(-2j / n_rot) * (freq_scale * (1 - g_j) + g_j)   (yarn)
  *     g_j = ext_factor * ramp(c(beta_fast), c(beta_slow), j)
  *     c(beta) = n_rot * ln(n_ctx_orig / (2 pi beta)) / (2 ln base)
  *     ramp(lo, hi, j) = 1 - clamp((j - lo) / max(0.001, hi - lo), 0, 1)
- * and the pair (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c) with c = cos(theta) * mscale,
- * s = sin(theta) * mscale.  Dims [0, d - n_rot) are left unchanged.  Plain RoPE over a
- * whole head is n_rot = d, yarn = 0, mscale = 1. */
+ * The pair (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c) with c = cos(theta) * mscale,
+ * s = sgn * sin(theta) * mscale, sgn = -1 for the inverse rotation ([ds4] Trace 2's
+ * `inverse` flag), else +1.  Dims [0, o) are left unchanged.  Plain RoPE over a whole
+ * head is n_rot = d, yarn = 0, mscale = 1, and the added fields zero.
+ * Tables ([Sophgo] Listings 1-2 gather precomputed cos / sin by position_ids): when
+ * cos_table and sin_table are set (device, float32 [table_rows, n_rot/2], 4-byte
+ * aligned), pair j of a token at position p takes c = cos_table[p][j] and
+ * s = sgn * sin_table[p][j] instead (base, yarn fields and mscale are then not used).  A
+ * token whose position lies outside [0, table_rows) gets NaN in its rotated dims (the
+ * library cannot report it; for k that row of the cache holds NaN). */
 typedef struct kvrope_rope_params {
     double base;        /* > 1 (10000 in the workloads) */
     int32_t n_rot;      /* even, 2 .. d */
@@ -85,6 +94,11 @@ typedef struct kvrope_rope_params {
     double beta_fast;   /* yarn: > 0 */
     double beta_slow;   /* yarn: > 0 */
     double mscale;      /* finite, > 0 */
+    int32_t pairing;    /* 0 = adjacent, 1 = half-split */
+    int32_t inverse;    /* 0 = forward, 1 = inverse rotation */
+    const float *cos_table; /* NULL, or device float32 [table_rows, n_rot / 2] */
+    const float *sin_table; /* NULL exactly when cos_table is */
+    int32_t table_rows;     /* >= 1 when the tables are set */
 } kvrope_rope_params;
 
 /* attn_rope_apply -- rotate x in place ([Sophgo] Listings 1-2: top.Rope(x, cos, sin) on

@@ -49,15 +49,42 @@ class KVRopeError(RuntimeError):
 
 
 class RopeParams(ctypes.Structure):
-    """Mirror of ``kvrope_rope_params``."""
+    """Mirror of ``kvrope_rope_params``.
+
+    ``with_variant`` sets the half-split pairing, the inverse rotation and the caller's
+    cos / sin tables (CUDA float32 tensors [rows, n_rot / 2]; the struct keeps them alive).
+    """
     _fields_ = [("base", ctypes.c_double), ("n_rot", ctypes.c_int32), ("yarn", ctypes.c_int32),
                 ("freq_scale", ctypes.c_double), ("ext_factor", ctypes.c_double),
                 ("n_ctx_orig", ctypes.c_int32), ("beta_fast", ctypes.c_double),
-                ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double)]
+                ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double),
+                ("pairing", ctypes.c_int32), ("inverse", ctypes.c_int32),
+                ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                ("table_rows", ctypes.c_int32)]
 
     @classmethod
     def plain(cls, n_rot: int = 128, base: float = 10000.0) -> "RopeParams":
         return cls(base, n_rot, 0, 1.0, 0.0, 4096, 32.0, 1.0, 1.0)
+
+    def with_variant(self, half_split: bool = False, inverse: bool = False, cos_table=None,
+                     sin_table=None) -> "RopeParams":
+        """A copy with the given pairing, direction and tables."""
+        r = RopeParams.from_buffer_copy(self)
+        r.pairing, r.inverse = int(half_split), int(inverse)
+        if (cos_table is None) != (sin_table is None):
+            raise ValueError("cos_table and sin_table go together")
+        if cos_table is not None:
+            for tt in (cos_table, sin_table):
+                if not (tt.is_cuda and tt.dtype == torch.float32 and tt.is_contiguous() and tt.dim() == 2
+                        and tt.shape == cos_table.shape and tt.shape[1] == self.n_rot // 2):
+                    raise ValueError("tables must be contiguous CUDA float32 [rows, n_rot / 2]")
+            r.cos_table, r.sin_table = cos_table.data_ptr(), sin_table.data_ptr()
+            r.table_rows = cos_table.shape[0]
+            r._keep = (cos_table, sin_table)
+        else:
+            r.cos_table = r.sin_table = None
+            r.table_rows = 0
+        return r
 
     @classmethod
     def yarn_tail(cls, n_rot: int = 64, base: float = 10000.0, factor: float = 4.0,

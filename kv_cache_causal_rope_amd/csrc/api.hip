@@ -25,6 +25,19 @@ int check_rope(const kvrope_rope_params *rp, int d)
         return KVROPE_ERR_NULL;
     if (rp->n_rot < 2 || rp->n_rot > d || (rp->n_rot & 1))
         return KVROPE_ERR_ROPE;
+    if ((rp->pairing != 0 && rp->pairing != 1) || (rp->inverse != 0 && rp->inverse != 1))
+        return KVROPE_ERR_ROPE;
+    if (rp->pairing == 1 && rp->n_rot % 32 != 0)
+        return KVROPE_ERR_ROPE;
+    if ((rp->cos_table == nullptr) != (rp->sin_table == nullptr))
+        return KVROPE_ERR_ROPE;
+    if (rp->cos_table) {
+        if (rp->table_rows < 1)
+            return KVROPE_ERR_ROPE;
+        if (!aligned4(rp->cos_table) || !aligned4(rp->sin_table))
+            return KVROPE_ERR_ALIGN;
+        return KVROPE_OK; // the computed-angle fields are not used
+    }
     if (!isfinite(rp->base) || rp->base <= 1.0)
         return KVROPE_ERR_ROPE;
     if (!finite_pos(rp->mscale))
@@ -51,7 +64,12 @@ kvrope::RopeTable rope_table(const kvrope_rope_params &rp, int d)
     kvrope::RopeTable tab;
     tab.n_pairs = rp.n_rot / 2;
     tab.off = d - rp.n_rot;
-    tab.mscale = rp.mscale;
+    tab.mscale = rp.cos_table ? 1.0 : rp.mscale;
+    tab.half = rp.pairing;
+    tab.sgn = rp.inverse ? -1.0 : 1.0;
+    tab.cos_t = rp.cos_table;
+    tab.sin_t = rp.sin_table;
+    tab.rows = rp.cos_table ? rp.table_rows : 0;
     const double two_pi = 6.283185307179586476925286766559;
     double lo = 0.0, hi = 0.0;
     if (rp.yarn) {
@@ -61,7 +79,7 @@ kvrope::RopeTable rope_table(const kvrope_rope_params &rp, int d)
     }
     for (int j = 0; j < kvrope::kMaxPairs; ++j) {
         double w = 0.0;
-        if (j < tab.n_pairs) {
+        if (j < tab.n_pairs && !rp.cos_table) {
             w = pow(rp.base, -2.0 * (double)j / (double)rp.n_rot);
             if (rp.yarn) {
                 double y = ((double)j - lo) / fmax(0.001, hi - lo);

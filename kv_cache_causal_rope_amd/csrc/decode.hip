@@ -108,60 +108,81 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, RopeT
     const int k1 = min(k0 + p.chunk, nk);
     const bool has_new = (len >= k0 && len < k1);
 
-    // ---- prologue: trig once per pair (fp64), shared by q heads and k
-    const double posd = (double)p.pos[u];
+    // ---- prologue: trig once per pair (fp64), shared by q heads and k (or the caller's
+    // table entries of the token's position; NaN when the table does not cover it)
+    const int posi = p.pos[u];
     if (tid < tab.n_pairs) {
         double s, co;
-        sincos(posd * tab.w[tid], &s, &co);
+        if (tab.cos_t) {
+            const bool in = posi >= 0 && posi < tab.rows;
+            co = in ? (double)tab.cos_t[(int64_t)posi * tab.n_pairs + tid] : __builtin_nan("");
+            s = in ? (double)tab.sin_t[(int64_t)posi * tab.n_pairs + tid] : __builtin_nan("");
+        } else {
+            sincos((double)posi * tab.w[tid], &s, &co);
+        }
         sm.cs[tid] = co * tab.mscale;
-        sm.sn[tid] = s * tab.mscale;
+        sm.sn[tid] = s * tab.mscale * tab.sgn;
     }
     __syncthreads();
     {
 #pragma clang fp contract(off)
-        // rotated q heads of this slice -> LDS (f16, nearest even); one thread per pair
+        // Pair `it` of a head: rotated pair j = it - off/2 when it >= off/2, with dims
+        // (off + 2j, off + 2j + 1) or, half-split, (off + j, off + j + n_pairs); below
+        // off/2 the pair (2 it, 2 it + 1) is copied.
         const int half_d = kHeadDim / 2;
+        auto dims = [&](int it, int &da, int &db) -> int {
+            const int j = it - (tab.off >> 1);
+            if (j < 0) {
+                da = 2 * it;
+                db = da + 1;
+            } else {
+                da = tab.half ? tab.off + j : tab.off + 2 * j;
+                db = tab.half ? da + tab.n_pairs : da + 1;
+            }
+            return j;
+        };
+        // rotated q heads of this slice -> LDS (f16, nearest even); one thread per pair
         for (int it = tid; it < GS * half_d; it += 256) {
             const int hl = it / half_d, pr = it % half_d;
-            const int d0 = 2 * pr;
+            int da, db;
+            const int j = dims(pr, da, db);
             uint16_t y0 = 0, y1 = 0;
             if (hl < nh) {
                 const uint16_t *qr = p.q + ((int64_t)u * p.hq + h0 + hl) * kHeadDim;
-                const uint16_t a0 = qr[d0], a1 = qr[d0 + 1];
+                const uint16_t a0 = qr[da], a1 = qr[db];
                 y0 = a0;
                 y1 = a1;
-                if (d0 >= tab.off) {
-                    const int j = (d0 - tab.off) >> 1;
+                if (j >= 0) {
                     const double x0 = h2d(a0), x1 = h2d(a1);
                     y0 = f64_to_f16_rne(x0 * sm.cs[j] - x1 * sm.sn[j]);
                     y1 = f64_to_f16_rne(x0 * sm.sn[j] + x1 * sm.cs[j]);
                 }
             }
-            sm.qh[hl][d0] = y0;
-            sm.qh[hl][d0 + 1] = y1;
+            sm.qh[hl][da] = y0;
+            sm.qh[hl][db] = y1;
         }
         if (has_new && tid < half_d) {
-            const int d0 = 2 * tid;
+            int da, db;
+            const int j = dims(tid, da, db);
             const uint16_t *kr = p.k + ((int64_t)u * p.hkv + g) * kHeadDim;
             const uint16_t *vr = p.v + ((int64_t)u * p.hkv + g) * kHeadDim;
-            uint16_t y0 = kr[d0], y1 = kr[d0 + 1];
-            if (d0 >= tab.off) {
-                const int j = (d0 - tab.off) >> 1;
+            uint16_t y0 = kr[da], y1 = kr[db];
+            if (j >= 0) {
                 const double x0 = h2d(y0), x1 = h2d(y1);
                 y0 = f64_to_f16_rne(x0 * sm.cs[j] - x1 * sm.sn[j]);
                 y1 = f64_to_f16_rne(x0 * sm.sn[j] + x1 * sm.cs[j]);
             }
-            sm.knew[d0] = y0;
-            sm.knew[d0 + 1] = y1;
-            sm.vnew[d0] = vr[d0];
-            sm.vnew[d0 + 1] = vr[d0 + 1];
+            sm.knew[da] = y0;
+            sm.knew[db] = y1;
+            sm.vnew[da] = vr[da];
+            sm.vnew[db] = vr[db];
             if (sl == 0) {
                 // append: row len of this unit's KV head g
                 const int64_t row = (((int64_t)u * p.hkv + g) * p.s_cap + len) * kHeadDim;
-                p.ck[row + d0] = y0;
-                p.ck[row + d0 + 1] = y1;
-                p.cv[row + d0] = vr[d0];
-                p.cv[row + d0 + 1] = vr[d0 + 1];
+                p.ck[row + da] = y0;
+                p.ck[row + db] = y1;
+                p.cv[row + da] = vr[da];
+                p.cv[row + db] = vr[db];
             }
         }
     }

@@ -30,6 +30,11 @@ struct RopeTable {
     double mscale;
     int n_pairs; // n_rot / 2
     int off;     // first rotated dim (d - n_rot)
+    int half;    // 1: pair j is dims (off + j, off + j + n_pairs); 0: (off + 2j, off + 2j + 1)
+    double sgn;  // sign of the sine: -1 for the inverse rotation
+    const float *cos_t; // caller tables [rows][n_pairs] (NULL: cos / sin of pos * w)
+    const float *sin_t;
+    int rows;
 };
 
 // fp64 -> IEEE binary16, round to nearest, ties to even, by bit manipulation.

@@ -81,6 +81,20 @@ constexpr int NSTAGE = 4;
 constexpr int VREG_B = NSTAGE * TILE_B; // V regions start after the four K regions
 constexpr int RD = 6;                  // operand reads in flight ahead of the MFMAs
 
+// How q is rotated beyond the per-slot angle rates and scales kept in LDS.  Slot dp of a
+// head is the dim pair (2 dp, 2 dp + 1) below off / 2; from off / 2 on it is rotated pair
+// j = dp - off / 2, whose dims are (off + 2 j, off + 2 j + 1), or, half-split,
+// (off + j, off + j + n_pairs).
+struct QRot {
+    const float *cos_t; // caller tables [rows][n_pairs] (NULL: computed angles)
+    const float *sin_t;
+    int rows;
+    int n_pairs;
+    int off2; // off / 2: the first rotated slot
+    int h16;  // half-split: n_pairs / 16 (1 .. 4); 0: adjacent pairs
+    float sgn; // sign of the sine (-1: inverse rotation)
+};
+
 struct PrefillParams {
     const uint16_t *q;
     const uint16_t *ck;
@@ -213,57 +227,114 @@ __device__ inline void store_v(const VRegs &r, char *lds, const uint32_t (&vst)[
     }
 }
 
-// q rotation: dims (2 dp, 2 dp + 1) of the lane's 8 dim steps (16 s + 8 hh .. + 7) by
-// fp32 trig of the fp64-reduced angle (revolutions wdim[dp] per position), scaled by
-// sdim[dp] and rounded to f16: the B operands of the S^T product.
-__device__ inline void rotate_q(half8 (&qop)[8], const u32x4 (&qin)[8], int qpos, int hh, const double *wdim,
-                                const float *sdim)
+// Factors (c, s) of slot dp at position qpos, times the slot's output scale sdim[dp]:
+// fp32 trig of the fp64-reduced angle (signed revolutions wdim[dp] per position, negative
+// for the inverse rotation; 0 for unrotated slots), or, with TAB, the caller's table entry
+// of a rotated slot (NaN for a position the table does not cover), the sine times the
+// rotation's sign.
+template <bool TAB>
+__device__ inline void slot_factor(int dp, int qpos, const double *wdim, const float *sdim, const QRot r,
+                                   float &cs, float &sn)
 {
-    const double posd = (double)qpos;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int dp0 = 8 * s + 4 * hh;
-        const u32x4 in = qin[s];
-        u32x4 hv;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp0 + m]);
-            const float sc = sdim[dp0 + m];
-            const float cs = __builtin_amdgcn_cosf(rf) * sc;
-            const float sn = __builtin_amdgcn_sinf(rf) * sc;
-            const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
-            const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
-            hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
-        }
-        qop[s] = __builtin_bit_cast(half8, hv);
+    const float sc = sdim[dp];
+    if (TAB && dp >= r.off2) {
+        const int j = dp - r.off2;
+        const bool in = qpos >= 0 && qpos < r.rows;
+        cs = in ? r.cos_t[(int64_t)qpos * r.n_pairs + j] * sc : __builtin_nanf("");
+        sn = in ? r.sin_t[(int64_t)qpos * r.n_pairs + j] * sc * r.sgn : __builtin_nanf("");
+    } else {
+        const float rf = (float)__builtin_amdgcn_fract((double)qpos * wdim[dp]);
+        cs = __builtin_amdgcn_cosf(rf) * sc;
+        sn = __builtin_amdgcn_sinf(rf) * sc;
     }
 }
 
+__device__ inline uint32_t rot_pack(float x0, float x1, float cs, float sn)
+{
+    const floatx2 y = {x0 * cs - x1 * sn, x0 * sn + x1 * cs};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
+}
+
+// Half-split rotation of block pair (s, s + H16) (dims 16 s + 8 hh + e and the same plus
+// n_pairs, for e = 0 .. 7): cs / sn of the eight pairs given.
+__device__ inline void rot_half_blocks(const u32x4 &a, const u32x4 &b, const float (&cs)[8], const float (&sn)[8],
+                                       half8 &ya, half8 &yb)
+{
+    u32x4 ha, hb;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float a0 = lo2f(a[w]), a1 = hi2f(a[w]), b0 = lo2f(b[w]), b1 = hi2f(b[w]);
+        const int e = 2 * w;
+        const floatx2 y0 = {a0 * cs[e] - b0 * sn[e], a1 * cs[e + 1] - b1 * sn[e + 1]};
+        const floatx2 y1 = {a0 * sn[e] + b0 * cs[e], a1 * sn[e + 1] + b1 * cs[e + 1]};
+        ha[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y0, half2v));
+        hb[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y1, half2v));
+    }
+    ya = __builtin_bit_cast(half8, ha);
+    yb = __builtin_bit_cast(half8, hb);
+}
+
+// q rotation, scaled and rounded to f16: the B operands of the S^T product.  The lane
+// holds dims 16 s + 8 hh .. + 7 of its query in qin[s].  Adjacent pairs: slot
+// 8 s + 4 hh + m is the lane's word m of block s.  Half-split (H16 = n_pairs / 16; the
+// rotated dims start at block 8 - 2 H16): a block below that is scaled per slot as
+// above; block s of the first rotated half and block s + H16 hold the two dims of slots
+// off / 2 + 16 (s - (8 - 2 H16)) + 8 hh + e.
+template <int H16, bool TAB>
+__device__ inline void rotate_q_t(half8 (&qop)[8], const u32x4 (&qin)[8], int qpos, int hh, const double *wdim,
+                                  const float *sdim, const QRot r)
+{
+    constexpr int S0 = H16 ? 8 - 2 * H16 : 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if (s < S0) {
+            const int dp0 = 8 * s + 4 * hh;
+            const u32x4 in = qin[s];
+            u32x4 hv;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                float cs, sn;
+                slot_factor<TAB>(dp0 + m, qpos, wdim, sdim, r, cs, sn);
+                hv[m] = rot_pack(lo2f(in[m]), hi2f(in[m]), cs, sn);
+            }
+            qop[s] = __builtin_bit_cast(half8, hv);
+        } else if (s < S0 + H16) {
+            const int dp0 = 8 * S0 + 16 * (s - S0) + 8 * hh;
+            float cs[8], sn[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                slot_factor<TAB>(dp0 + e, qpos, wdim, sdim, r, cs[e], sn[e]);
+            rot_half_blocks(qin[s], qin[s + H16], cs, sn, qop[s], qop[s + H16]);
+        }
+    }
+}
+
+
+
 // The rotation factors of a workgroup's tokens, shared by the query heads of a group:
-// entry (token k, dim pairs 4 g .. 4 g + 3) holds {cos, sin} of each pair, times the
-// pair's output scale, 32 bytes at byte (g * ntok + k) * 32 (a row of consecutive
-// tokens per pair group, so the lanes of a wave read consecutive entries).
+// entry (token k, slots 4 g .. 4 g + 3) holds {cos, sin} of each slot as slot_factor
+// gives them, 32 bytes at byte (g * ntok + k) * 32 (a row of consecutive tokens per slot
+// group, so the lanes of a wave read consecutive entries).
 constexpr int TAB_B = 2 * TILE_B; // LDS byte offset: the K regions of stages 2 and 3
 
 // Fill the table for ntok tokens (32 or 64): thread tid computes token k = tid % ntok at
 // position tpos (that token's), pair groups (tid / ntok) * (ntok / 32) + 0 .. ntok / 32 - 1.
 // The factors are the ones rotate_q computes.
+template <bool TAB>
 __device__ inline void fill_rot_table(char *lds, int tpos, int ntok, int tid, const double *wdim,
-                                      const float *sdim)
+                                      const float *sdim, const QRot r)
 {
     const int k = tid % ntok;
     const int per = ntok / QB;
-    const double posd = (double)tpos;
     for (int e = 0; e < per; ++e) {
         const int g = (tid / ntok) * per + e;
         floatx4 f[2];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int dp = 4 * g + m;
-            const float rf = (float)__builtin_amdgcn_fract(posd * wdim[dp]);
-            const float sc = sdim[dp];
-            f[m >> 1][2 * (m & 1)] = __builtin_amdgcn_cosf(rf) * sc;
-            f[m >> 1][2 * (m & 1) + 1] = __builtin_amdgcn_sinf(rf) * sc;
+            float cs, sn;
+            slot_factor<TAB>(4 * g + m, tpos, wdim, sdim, r, cs, sn);
+            f[m >> 1][2 * (m & 1)] = cs;
+            f[m >> 1][2 * (m & 1) + 1] = sn;
         }
         floatx4 *dst = reinterpret_cast<floatx4 *>(lds + TAB_B + (g * ntok + k) * 32);
         dst[0] = f[0];
@@ -271,28 +342,37 @@ __device__ inline void fill_rot_table(char *lds, int tpos, int ntok, int tid, co
     }
 }
 
-// rotate_q with the factors of table token k: dims 16 s + 8 hh + 2 m + {0, 1} are pair
-// 4 (2 s + hh) + m.
-__device__ inline void rotate_q_tab(half8 (&qop)[8], const u32x4 (&qin)[8], const char *lds, int ntok, int k,
-                                    int hh)
+// rotate_q with the factors of table token k (slots as in rotate_q_t)
+template <int H16>
+__device__ inline void rotate_q_tab_t(half8 (&qop)[8], const u32x4 (&qin)[8], const char *lds, int ntok, int k,
+                                      int hh)
 {
+    constexpr int S0 = H16 ? 8 - 2 * H16 : 8;
+    auto entry = [&](int g) { return reinterpret_cast<const floatx4 *>(lds + TAB_B + (g * ntok + k) * 32); };
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const floatx4 *src = reinterpret_cast<const floatx4 *>(lds + TAB_B + ((2 * s + hh) * ntok + k) * 32);
-        const floatx4 f0 = src[0], f1 = src[1];
-        const float cs[4] = {f0[0], f0[2], f1[0], f1[2]};
-        const float sn[4] = {f0[1], f0[3], f1[1], f1[3]};
-        const u32x4 in = qin[s];
-        u32x4 hv;
+        if (s < S0) {
+            const floatx4 *src = entry(2 * s + hh);
+            const floatx4 f0 = src[0], f1 = src[1];
+            const float cs[4] = {f0[0], f0[2], f1[0], f1[2]};
+            const float sn[4] = {f0[1], f0[3], f1[1], f1[3]};
+            const u32x4 in = qin[s];
+            u32x4 hv;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float x0 = lo2f(in[m]), x1 = hi2f(in[m]);
-            const floatx2 y = {x0 * cs[m] - x1 * sn[m], x0 * sn[m] + x1 * cs[m]};
-            hv[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, half2v));
+            for (int m = 0; m < 4; ++m)
+                hv[m] = rot_pack(lo2f(in[m]), hi2f(in[m]), cs[m], sn[m]);
+            qop[s] = __builtin_bit_cast(half8, hv);
+        } else if (s < S0 + H16) {
+            const int g0 = (8 * S0 + 16 * (s - S0) + 8 * hh) / 4;
+            const floatx4 *p0 = entry(g0), *p1 = entry(g0 + 1);
+            const floatx4 f0 = p0[0], f1 = p0[1], f2 = p1[0], f3 = p1[1];
+            const float cs[8] = {f0[0], f0[2], f1[0], f1[2], f2[0], f2[2], f3[0], f3[2]};
+            const float sn[8] = {f0[1], f0[3], f1[1], f1[3], f2[1], f2[3], f3[1], f3[3]};
+            rot_half_blocks(qin[s], qin[s + H16], cs, sn, qop[s], qop[s + H16]);
         }
-        qop[s] = __builtin_bit_cast(half8, hv);
     }
 }
+
 
 // Rare path.  The fast path keeps each row's reference max from its first tile; when a
 // later key scores 2^16 or more above it, an f16 probability overflows and the row sum
@@ -300,8 +380,10 @@ __device__ inline void rotate_q_tab(half8 (&qop)[8], const u32x4 (&qin)[8], cons
 // max moved on every tile that exceeds it (so no probability exceeds 1): plainly, one
 // tile at a time through LDS stage 0, each wave its own item.  Not inlined, so that its
 // registers do not weigh on the fast path.
+template <int H16, bool TAB>
 __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char *lds, const double *wdim,
-                                                     const float *sdim, int u, int g, int wk, int hist)
+                                                     const float *sdim, int u, int g, int wk, int hist,
+                                                     const QRot rot)
 {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -328,7 +410,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     for (int s = 0; s < 8; ++s)
         qin[s] = ld16(qrow + 16 * s + 8 * hh);
     half8 qop[8];
-    rotate_q(qop, qin, p.pos[(int64_t)u * p.t + iq], hh, wdim, sdim);
+    rotate_q_t<H16, TAB>(qop, qin, p.pos[(int64_t)u * p.t + iq], hh, wdim, sdim, rot);
 
     uint32_t vst[8];
 #pragma unroll
@@ -420,7 +502,11 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     }
 }
 
-__global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab)
+// H16: the pairing of q's rotated dims, as in rotate_q_t; TAB: factors from the caller's
+// tables.  One kernel per variant keeps the other variants' code out of the fast path's
+// register allocation.
+template <int H16, bool TAB>
+__global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab, QRot rot)
 {
     __shared__ __align__(16) char lds[2 * NSTAGE * TILE_B];
     __shared__ double wdim[kMaxPairs]; // revolutions per position of dim pair dp (0: unrotated)
@@ -446,7 +532,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     if (tid < kMaxPairs) {
         const bool rot_t = 2 * tid >= tab.off;
         const float sl2 = p.scale_log2;
-        wdim[tid] = rot_t ? tab.wrev[tid - (tab.off >> 1)] : 0.0;
+        wdim[tid] = rot_t ? tab.sgn * tab.wrev[tid - (tab.off >> 1)] : 0.0;
         sdim[tid] = rot_t ? (float)tab.mscale * sl2 : sl2;
     }
     if (tid == 0)
@@ -566,11 +652,11 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         half8 qop[8];
         if (ntok <= 2 * QB) {
             wg_barrier(); // every wave has read its previous unit's output rows back
-            fill_rot_table(lds, tpos, ntok, tid, wdim, sdim);
+            fill_rot_table<TAB>(lds, tpos, ntok, tid, wdim, sdim, rot);
             wg_barrier();
-            rotate_q_tab(qop, qin, lds, ntok, (tb - tb_first) * QB + c, hh);
+            rotate_q_tab_t<H16>(qop, qin, lds, ntok, (tb - tb_first) * QB + c, hh);
         } else {
-            rotate_q(qop, qin, qpos, hh, wdim, sdim);
+            rotate_q_t<H16, TAB>(qop, qin, qpos, hh, wdim, sdim, rot);
         }
 
         // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
@@ -820,7 +906,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             ovf_unit = v;
         wg_barrier();
         if (ovf_unit == v) {
-            exact_unit(p, lds, wdim, sdim, u, g, wk, hist);
+            // (without tables the rotation needs nothing beyond LDS: no live kernel arguments)
+            exact_unit<H16, TAB>(p, lds, wdim, sdim, u, g, wk, hist, TAB ? rot : QRot{});
             continue;
         }
 
@@ -906,6 +993,14 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
         return hipErrorInvalidValue;
     p.units = (int)units;
     p.scale_log2 = (float)((double)s.scale * 1.4426950408889634);
+    QRot rot;
+    rot.cos_t = tab.cos_t;
+    rot.sin_t = tab.sin_t;
+    rot.rows = tab.rows;
+    rot.n_pairs = tab.n_pairs;
+    rot.off2 = tab.off >> 1;
+    rot.h16 = tab.half ? tab.n_pairs / 16 : 0;
+    rot.sgn = (float)tab.sgn;
     // one workgroup per compute unit (the LDS ring takes most of a CU's LDS)
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -918,7 +1013,14 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
 
     if (ev_before)
         (void)hipEventRecord(ev_before, stream);
-    hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p, tab);
+    using Kernel = void (*)(PrefillParams, RopeTable, QRot);
+    static const Kernel kernels[2][5] = {
+        {prefill_attn_kernel<0, false>, prefill_attn_kernel<1, false>, prefill_attn_kernel<2, false>,
+         prefill_attn_kernel<3, false>, prefill_attn_kernel<4, false>},
+        {prefill_attn_kernel<0, true>, prefill_attn_kernel<1, true>, prefill_attn_kernel<2, true>,
+         prefill_attn_kernel<3, true>, prefill_attn_kernel<4, true>}};
+    hipLaunchKernelGGL(kernels[tab.cos_t ? 1 : 0][rot.h16], dim3((unsigned)blocks), dim3(NT), 0, stream, p, tab,
+                       rot);
     hipError_t err = hipGetLastError();
     if (ev_after)
         (void)hipEventRecord(ev_after, stream);

@@ -1,11 +1,13 @@
 // rope_append.hip -- rotary embedding and KV-cache append kernels (gfx950).
 //
 // Rotation ("ds4.c study notes", Part 4 sec. 1, Trace 2): pair j of a head holds dims
-// (off + 2j, off + 2j + 1), off = d - n_rot; with theta = pos * w[j] and
-// c = cos(theta) * mscale, s = sin(theta) * mscale the pair (x0, x1) becomes
-// (x0 c - x1 s, x0 s + x1 c).  These kernels evaluate it in fp64 and round once to f16
-// (nearest even), so a rotated K row in the cache is the correctly rounded f16 of the
-// exact rotation.  The angle is taken in turns (pos * w[j] / 2 pi, reduced exactly to a
+// (off + 2j, off + 2j + 1), off = d - n_rot (or, half-split, (off + j, off + j + n_rot/2));
+// with theta = pos * w[j], c = cos(theta) * mscale and s = sgn * sin(theta) * mscale
+// (sgn = -1 for the inverse rotation) the pair (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c).
+// With caller tables (the Sophgo MLIR-based LLM compilation paper, Listings 1-2: cos / sin
+// gathered by position_ids) c and s / sgn are the table entries of the token's position.
+// These kernels evaluate it in fp64 and round once to f16 (nearest even), so a rotated K
+// row in the cache is the correctly rounded f16 of the exact rotation.  The angle is taken in turns (pos * w[j] / 2 pi, reduced exactly to a
 // fraction of a turn) and its sine and cosine come from Taylor series on at most an
 // eighth of a turn: within a few 1e-16 of fp64 sin / cos of pos * w[j], at a fraction
 // of their cost.
@@ -70,22 +72,53 @@ __device__ inline void sincos_turns(double r, double &s, double &c)
     }
 }
 
-__device__ inline void chunk_trig(int c, double pos, const RopeTable &tab, double (&cs)[4],
-                                  double (&sn)[4])
+// c and s of rotated pair j at position pos (NaN when a table does not cover pos)
+__device__ inline void pair_factor(int j, int pos, const RopeTable &tab, double &c, double &s)
 {
 #pragma clang fp contract(off)
+    if (tab.cos_t) {
+        if (pos >= 0 && pos < tab.rows) {
+            c = (double)tab.cos_t[(int64_t)pos * tab.n_pairs + j];
+            s = (double)tab.sin_t[(int64_t)pos * tab.n_pairs + j] * tab.sgn;
+        } else {
+            c = s = __builtin_nan("");
+        }
+    } else {
+        double sv, cv;
+        sincos_turns((double)pos * tab.wrev[j], sv, cv);
+        c = cv * tab.mscale;
+        s = sv * tab.mscale * tab.sgn;
+    }
+}
+
+// adjacent pairing: the factors of the four pairs of chunk c (identity before `off`)
+__device__ inline void chunk_trig(int c, int pos, const RopeTable &tab, double (&cs)[4],
+                                  double (&sn)[4])
+{
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int dim = 8 * c + 2 * m;
         cs[m] = 1.0;
         sn[m] = 0.0;
-        if (dim >= tab.off) {
-            const int j = (dim - tab.off) >> 1;
-            double s, co;
-            sincos_turns(pos * tab.wrev[j], s, co);
-            cs[m] = co * tab.mscale;
-            sn[m] = s * tab.mscale;
-        }
+        if (dim >= tab.off)
+            pair_factor((dim - tab.off) >> 1, pos, tab, cs[m], sn[m]);
+    }
+}
+
+// half-split pairing: chunk c0 of the first rotated half and its partner chunk
+// c0 + n_pairs / 8 hold the two dims of pairs 8 (c0 - off / 8) + e, e = 0 .. 7
+__device__ inline void rotate_half_chunks(const uint16_t (&a)[8], const uint16_t (&b)[8], uint16_t (&ya)[8],
+                                          uint16_t (&yb)[8], int j0, int pos, const RopeTable &tab)
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        double c, s;
+        pair_factor(j0 + e, pos, tab, c, s);
+        const double x0 = h2d(a[e]);
+        const double x1 = h2d(b[e]);
+        ya[e] = f64_to_f16_rne_dev(x0 * c - x1 * s);
+        yb[e] = f64_to_f16_rne_dev(x0 * s + x1 * c);
     }
 }
 
@@ -94,6 +127,14 @@ union Chunk16 {
     uint16_t h[8];
 };
 
+// 16-byte chunks per row a thread of the rotation kernels starts from: every chunk of
+// the rotated region (adjacent pairs), or its first half (half-split pairs, the thread
+// also taking the partner chunk)
+inline int rope_chunks(const RopeTable &tab)
+{
+    return tab.half ? tab.n_pairs >> 3 : (kHeadDim >> 3) - (tab.off >> 3);
+}
+
 // x[rows, h, 128] rotated in place; one thread per (row, 16-byte chunk of the rotated
 // region), looping over the heads so the trig is shared by all heads of a row.
 __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict__ x,
@@ -101,14 +142,28 @@ __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict_
                                                            int64_t rows, int h, RopeTable tab)
 {
     const int first_chunk = tab.off >> 3;
-    const int nchunks = (kHeadDim >> 3) - first_chunk;
+    const int nchunks = tab.half ? tab.n_pairs >> 3 : (kHeadDim >> 3) - first_chunk;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= rows * nchunks)
         return;
     const int c = first_chunk + (int)(idx % nchunks);
     const int64_t r = idx / nchunks;
+    const int pos = positions[r];
+    if (tab.half) {
+        const int c2 = c + (tab.n_pairs >> 3);
+        for (int hh = 0; hh < h; ++hh) {
+            uint4 *p = reinterpret_cast<uint4 *>(x + (r * h + hh) * kHeadDim);
+            Chunk16 a, b, ya, yb;
+            a.v = p[c];
+            b.v = p[c2];
+            rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab);
+            p[c] = ya.v;
+            p[c2] = yb.v;
+        }
+        return;
+    }
     double cs[4], sn[4];
-    chunk_trig(c, (double)positions[r], tab, cs, sn);
+    chunk_trig(c, pos, tab, cs, sn);
     for (int hh = 0; hh < h; ++hh) {
         uint4 *p = reinterpret_cast<uint4 *>(x + (r * h + hh) * kHeadDim) + c;
         Chunk16 in, out;
@@ -166,10 +221,34 @@ __global__ void __launch_bounds__(256) rope_append_kernel(
     const int len = lens ? lens[u] : 0;
     if (len < 0 || len > max_len)
         return;
+    if (tab.half) {
+        // chunks before `off` copy K; a first-half chunk rotates with its partner and
+        // writes both; a second-half chunk only copies V
+        const int first_chunk = tab.off >> 3, h8 = tab.n_pairs >> 3;
+        const int pos = positions[ti];
+        for (int g = 0; g < hkv; ++g) {
+            const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
+            const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
+            const uint4 *ks = reinterpret_cast<const uint4 *>(k + src);
+            uint4 *kd = reinterpret_cast<uint4 *>(cache_k + dst);
+            if (c < first_chunk) {
+                kd[c] = ks[c];
+            } else if (c < first_chunk + h8) {
+                Chunk16 a, b, ya, yb;
+                a.v = ks[c];
+                b.v = ks[c + h8];
+                rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab);
+                kd[c] = ya.v;
+                kd[c + h8] = yb.v;
+            }
+            reinterpret_cast<uint4 *>(cache_v + dst)[c] = reinterpret_cast<const uint4 *>(v + src)[c];
+        }
+        return;
+    }
     double cs[4], sn[4];
     const bool rotated = 8 * c + 7 >= tab.off;
     if (rotated)
-        chunk_trig(c, (double)positions[ti], tab, cs, sn);
+        chunk_trig(c, positions[ti], tab, cs, sn);
     for (int g = 0; g < hkv; ++g) {
         const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
         const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
@@ -191,8 +270,7 @@ inline unsigned grid_for(int64_t threads, int block) { return (unsigned)((thread
 hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int h,
                                const RopeTable &tab, hipStream_t stream)
 {
-    const int nchunks = (kHeadDim >> 3) - (tab.off >> 3);
-    const int64_t threads = rows * nchunks;
+    const int64_t threads = rows * rope_chunks(tab);
     if (threads == 0)
         return hipSuccess;
     hipLaunchKernelGGL(rope_inplace_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
