@@ -41,17 +41,17 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 265.946e6,
-        "src": ("aafa3b615108c3eb3ea0c7dcc2f062d5f48404d6a19e97a121b8e10e1af543f2",
-                "16d1b200f8085a56e2d1747d4107f847c84ac804d3a328d0352dbb5dd12f2d35")},
+        "bytes": 267.086e6,
+        "src": ("4bb063631012e789141dc4ccfe58075e3f27c878de7dfdadd951061f9ed0eb54",
+                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f")},
     "decode_split:qwen1p5b_decode_l4096_b32": {
-        "bytes": 2.83169e9,
-        "src": ("0e827424de0e7e6905cc1a0a1f7ba89cbabc21d4a17de32473e8efcf9a8819aa",
-                "16d1b200f8085a56e2d1747d4107f847c84ac804d3a328d0352dbb5dd12f2d35")},
+        "bytes": 2.83173e9,
+        "src": ("4a1e5b7edde7d82f6a74f4594169dd786604aa0228b28f37a59698b44ab43b7f",
+                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f")},
     "decode_split:yarn_decode_l32k_b64": {
-        "bytes": 23.03676e9,
-        "src": ("0e827424de0e7e6905cc1a0a1f7ba89cbabc21d4a17de32473e8efcf9a8819aa",
-                "16d1b200f8085a56e2d1747d4107f847c84ac804d3a328d0352dbb5dd12f2d35")},
+        "bytes": 23.03665e9,
+        "src": ("4a1e5b7edde7d82f6a74f4594169dd786604aa0228b28f37a59698b44ab43b7f",
+                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f")},
 }
 KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_split": "decode.hip"}
 
