@@ -139,6 +139,23 @@ int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *
                     void *out, int n, int t, int hq, int hkv, int d, int s_cap, double scale,
                     const kvrope_rope_params *rp, void *stream);
 
+/* attn_prefill_kv_varlen -- attn_prefill_kv over a batch whose units bring different
+ * numbers of new tokens (continuous batching of resumed conversations; the chunked
+ * prefill of [Sophgo] Listing 2 per sequence, history lengths already per unit).
+ *   new_lens  device, int32 [n]: unit u's new tokens are rows 0 .. new_lens[u] - 1 of its
+ *             q, k, v, positions (all padded to t rows); 0 <= new_lens[u] <= t.
+ * Unit u computes exactly what attn_prefill_kv computes for that unit alone with
+ * t = new_lens[u]: cache rows [hist_lens[u], hist_lens[u] + new_lens[u]) are written and
+ * out rows 0 .. new_lens[u] - 1.  Padding rows of out and every other cache row are left
+ * as they were; padding rows of q, k, v and positions may hold anything (they are read
+ * but never used).  A unit with new_lens[u] outside [0, t] is treated like an invalid
+ * history length: no cache row written, NaN in all t of its out rows.  new_lens may not be
+ * NULL (KVROPE_ERR_NULL) unless n * t == 0; everything else as for attn_prefill_kv. */
+int attn_prefill_kv_varlen(const void *q, const void *k, const void *v, const int32_t *positions,
+                           void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
+                           const int32_t *new_lens, void *out, int n, int t, int hq, int hkv, int d,
+                           int s_cap, double scale, const kvrope_rope_params *rp, void *stream);
+
 /* attn_decode -- one new token per unit ([Sophgo] sec. 4.1 decode; [Buddy] sec.
  * 6.4.5-6.4.6).
  *   q    [n, 1, hq, d] (= [n, hq, d]);  k, v  [n, 1, hkv, d];  positions [n]

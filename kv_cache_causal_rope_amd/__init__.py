@@ -37,7 +37,7 @@ KVROPE_OP_DECODE = 1
 
 # every symbol include/kvrope.h declares
 EXPORTS = ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
-           "attn_decode", "kvrope_workspace_size", "kvrope_status_string",
+           "attn_prefill_kv_varlen", "attn_decode", "kvrope_workspace_size", "kvrope_status_string",
            "kvrope_last_hip_error", "kvrope_set_profile_events", "kvrope_f64_to_f16",
            "kvrope_probe_stream", "kvrope_probe_mfma"]
 
@@ -132,6 +132,8 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill.argtypes = [_P] * 7 + [_I] * 6 + [ctypes.c_double, rp, _P]
     L.attn_prefill_kv.argtypes = ([_P] * 7 + [_I, _P] + [_I] * 6 +
                                   [ctypes.c_double, rp, _P])
+    L.attn_prefill_kv_varlen.argtypes = ([_P] * 7 + [_I, _P, _P] + [_I] * 6 +
+                                         [ctypes.c_double, rp, _P])
     L.attn_decode.argtypes = ([_P] * 7 + [_I, _P] + [_I] * 5 +
                               [ctypes.c_double, rp, _P, ctypes.c_size_t, _P])
     L.kvrope_workspace_size.argtypes = [_I] * 7
@@ -145,7 +147,7 @@ def lib() -> ctypes.CDLL:
     L.kvrope_probe_stream.argtypes = [_P, _P, _P] + [_I] * 6 + [_P, _P]
     L.kvrope_probe_mfma.argtypes = [_I, _I, _P, _P]
     for rtn in ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
-                "attn_decode", "kvrope_set_profile_events", "kvrope_probe_stream",
+                "attn_prefill_kv_varlen", "attn_decode", "kvrope_set_profile_events", "kvrope_probe_stream",
                 "kvrope_probe_mfma"]:
         getattr(L, rtn).restype = _I
     _lib = L
@@ -291,6 +293,26 @@ def prefill_kv(q, k, v, positions, cache_k, cache_v, hist_lens, max_hist: int, r
                                  _ptr(cache_v), _ptr(hist_lens), int(max_hist), _ptr(out), n, t,
                                  hq, hkv, d, s_cap, float(scale), ctypes.byref(rope),
                                  _stream(stream)))
+    return out
+
+
+def prefill_kv_varlen(q, k, v, positions, cache_k, cache_v, hist_lens, new_lens, max_hist: int,
+                      rope: RopeParams, scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """prefill_kv where unit u brings new_lens[u] <= t new tokens (rows past it are padding:
+    not appended, their out rows left as they were)."""
+    n, t, hq, hkv, d, s_cap = _attn_shapes(q, k, v, cache_k, cache_v)
+    _i32("positions", positions, (n, t))
+    _i32("hist_lens", hist_lens, (n,))
+    _i32("new_lens", new_lens, (n,))
+    if out is None:
+        out = torch.zeros_like(q)
+    _f16("out", out, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().attn_prefill_kv_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(cache_k),
+                                        _ptr(cache_v), _ptr(hist_lens), int(max_hist), _ptr(new_lens),
+                                        _ptr(out), n, t, hq, hkv, d, s_cap, float(scale),
+                                        ctypes.byref(rope), _stream(stream)))
     return out
 
 

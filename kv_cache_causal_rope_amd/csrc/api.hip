@@ -205,10 +205,13 @@ int kv_cache_append(void *cache_k, void *cache_v, const void *k, const void *v,
                                             lens, max_len, n, t, hkv, s_cap, static_cast<hipStream_t>(stream)));
 }
 
-int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *positions,
+namespace {
+
+// attn_prefill_kv and attn_prefill_kv_varlen (new_lens NULL: t new tokens per unit)
+int prefill_kv_impl(const void *q, const void *k, const void *v, const int32_t *positions,
                     void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
-                    void *out, int n, int t, int hq, int hkv, int d, int s_cap, double scale,
-                    const kvrope_rope_params *rp, void *stream)
+                    const int32_t *new_lens, void *out, int n, int t, int hq, int hkv, int d, int s_cap,
+                    double scale, const kvrope_rope_params *rp, void *stream)
 {
     if (n < 0 || t < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || d != kvrope::kHeadDim || s_cap < 1)
         return KVROPE_ERR_SHAPE;
@@ -225,7 +228,7 @@ int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *
         return KVROPE_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(history_k) ||
         !aligned16(history_v) || !aligned16(out) || !aligned4(positions) ||
-        (hist_lens && !aligned4(hist_lens)))
+        (hist_lens && !aligned4(hist_lens)) || (new_lens && !aligned4(new_lens)))
         return KVROPE_ERR_ALIGN;
     const int G = hq / hkv;
     if ((int64_t)n * hkv * G * ((t + 31) / 32) > kMaxGrid || (int64_t)n * t * 16 / 256 > kMaxGrid)
@@ -238,13 +241,35 @@ int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *
     uint16_t *cv = static_cast<uint16_t *>(history_v);
     hipError_t e = kvrope::launch_rope_append(ck, cv, static_cast<const uint16_t *>(k),
                                               static_cast<const uint16_t *>(v), positions, hist_lens,
-                                              max_hist, n, t, hkv, s_cap, tab, s);
+                                              new_lens, max_hist, n, t, hkv, s_cap, tab, s);
     if (e != hipSuccess)
         return hip_status(e);
     kvrope::PrefillShape ps{n, t, hq, hkv, s_cap, max_hist, (float)scale};
     return hip_status(kvrope::launch_prefill_attention(static_cast<const uint16_t *>(q), ck, cv, positions,
-                                                       hist_lens, static_cast<uint16_t *>(out), ps, tab, s,
-                                                       eb, ea));
+                                                       hist_lens, new_lens, static_cast<uint16_t *>(out), ps,
+                                                       tab, s, eb, ea));
+}
+
+} // namespace
+
+int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *positions,
+                    void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
+                    void *out, int n, int t, int hq, int hkv, int d, int s_cap, double scale,
+                    const kvrope_rope_params *rp, void *stream)
+{
+    return prefill_kv_impl(q, k, v, positions, history_k, history_v, hist_lens, max_hist, nullptr, out, n, t,
+                           hq, hkv, d, s_cap, scale, rp, stream);
+}
+
+int attn_prefill_kv_varlen(const void *q, const void *k, const void *v, const int32_t *positions,
+                           void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
+                           const int32_t *new_lens, void *out, int n, int t, int hq, int hkv, int d,
+                           int s_cap, double scale, const kvrope_rope_params *rp, void *stream)
+{
+    if (!new_lens && (int64_t)n * t > 0)
+        return KVROPE_ERR_NULL;
+    return prefill_kv_impl(q, k, v, positions, history_k, history_v, hist_lens, max_hist, new_lens, out, n,
+                           t, hq, hkv, d, s_cap, scale, rp, stream);
 }
 
 int attn_prefill(const void *q, const void *k, const void *v, const int32_t *positions,

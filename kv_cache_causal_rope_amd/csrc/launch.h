@@ -17,9 +17,10 @@ hipError_t launch_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k
                          const uint16_t *v, const int32_t *lens, int max_len, int n, int t,
                          int hkv, int s_cap, hipStream_t stream);
 
+// new_lens may be NULL (t rows per unit); rows i >= new_lens[u] are not appended
 hipError_t launch_rope_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,
                               const uint16_t *v, const int32_t *positions, const int32_t *lens,
-                              int max_len, int n, int t, int hkv, int s_cap,
+                              const int32_t *new_lens, int max_len, int n, int t, int hkv, int s_cap,
                               const RopeTable &tab, hipStream_t stream);
 
 struct PrefillShape {
@@ -28,10 +29,11 @@ struct PrefillShape {
 };
 
 // Causal GQA flash attention over the caches (rows already appended), with q rotated in
-// the kernel's prologue.  lens may be NULL (all zero).
+// the kernel's prologue.  lens may be NULL (all zero); new_lens may be NULL (t each).
 hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
                                     const uint16_t *cache_v, const int32_t *positions,
-                                    const int32_t *lens, uint16_t *out, const PrefillShape &s,
+                                    const int32_t *lens, const int32_t *new_lens, uint16_t *out,
+                                    const PrefillShape &s,
                                     const RopeTable &tab, hipStream_t stream,
                                     hipEvent_t ev_before, hipEvent_t ev_after);
 

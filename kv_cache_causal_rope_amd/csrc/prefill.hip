@@ -101,6 +101,7 @@ struct PrefillParams {
     const uint16_t *cv;
     const int32_t *pos;
     const int32_t *lens;
+    const int32_t *new_lens; // new tokens per unit (NULL: t each); rows past it are padding
     uint16_t *out;
     int n, t, hq, hkv, s_cap, max_hist;
     int G;       // query heads per KV head
@@ -383,7 +384,7 @@ __device__ inline void rotate_q_tab_t(half8 (&qop)[8], const u32x4 (&qin)[8], co
 template <int H16, bool TAB>
 __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char *lds, const double *wdim,
                                                      const float *sdim, int u, int g, int wk, int hist,
-                                                     const QRot rot)
+                                                     int tu, const QRot rot)
 {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,7 +397,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     const int tb = my_item / p.G;
     const int h = g * p.G + (my_item - tb * p.G);
     const int i0 = tb * QB, i = i0 + c;
-    const int kend = hist + min((last_item / p.G + 1) * QB, p.t);
+    const int kend = hist + min((last_item / p.G + 1) * QB, tu);
     const int klast = kend - 1;
     const int ntiles = (kend + KT - 1) / KT;
     const int qlimit = hist + i;
@@ -488,7 +489,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
         wg_barrier(); // stage 0 is reloaded next
     }
     const float inv = 1.f / half_sum(l_run);
-    if (wave_valid && i < p.t) {
+    if (wave_valid && i < tu) {
         uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
@@ -558,11 +559,12 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const int h = g * p.G + (my_item - tb * p.G);
         const int i0 = tb * QB;
         const int i = i0 + c;
-        const bool row_valid = wave_valid && i < p.t;
-
         const int hist = p.lens ? p.lens[u] : 0;
-        if (hist < 0 || hist > p.max_hist) {
-            // invalid history length: no cache was written for this unit; report NaN
+        const int tu = p.new_lens ? p.new_lens[u] : p.t; // this unit's new tokens
+        if (hist < 0 || hist > p.max_hist || tu < 0 || tu > p.t) {
+            // invalid history or new-token count: no cache was written for this unit; report
+            // NaN in every row
+            const bool row_valid = wave_valid && i < p.t;
             if (row_valid && hh == 0) {
                 uint16_t *orow = p.out + (((int64_t)u * p.t + i) * p.hq + h) * kHeadDim;
                 for (int d = 0; d < kHeadDim; ++d)
@@ -570,11 +572,15 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
             continue; // uniform over the workgroup: hist belongs to the unit
         }
+        const int tb_first = (wk * NW) / p.G;
+        if (tb_first * QB >= tu)
+            continue; // every row of the unit is padding (uniform over the workgroup)
+        const bool row_valid = wave_valid && i < tu;
         const int tb_last = last_item / p.G;
-        const int kend = hist + min((tb_last + 1) * QB, p.t); // keys the workgroup needs
+        const int kend = hist + min((tb_last + 1) * QB, tu); // keys the workgroup needs
         const int klast = kend - 1;
         const int ntiles = (kend + KT - 1) / KT;
-        const int kend_w = hist + min(i0 + QB, p.t);        // keys this wave needs
+        const int kend_w = hist + min(i0 + QB, tu);         // keys this wave needs
         const int qlimit = hist + i;                         // last visible key of the lane's query
 
         const char *kbase = reinterpret_cast<const char *>(p.ck + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
@@ -633,7 +639,6 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const int qpos = p.pos[(int64_t)u * p.t + iq];
         // position of this thread's token of the unit's rotation table (see below; rows
         // past t take row t - 1's), loaded first so that it arrives first
-        const int tb_first = (wk * NW) / p.G;
         const int ntok = (tb_last - tb_first + 1) * QB;
         const int tpos = p.pos[(int64_t)u * p.t + min(tb_first * QB + tid % ntok, p.t - 1)];
         u32x4 qin[8];
@@ -902,12 +907,12 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // An f16 probability past its range made a row sum infinite (or a NaN input made
         // it NaN): the workgroup recomputes the unit on the exact path.  The flag holds the
         // unit, so it never needs clearing.
-        if (__builtin_amdgcn_ballot_w64(!(lsum[0] <= 3.0e38f)) != 0 && lane == 0)
+        if (__builtin_amdgcn_ballot_w64(row_valid && !(lsum[0] <= 3.0e38f)) != 0 && lane == 0)
             ovf_unit = v;
         wg_barrier();
         if (ovf_unit == v) {
             // (without tables the rotation needs nothing beyond LDS: no live kernel arguments)
-            exact_unit<H16, TAB>(p, lds, wdim, sdim, u, g, wk, hist, TAB ? rot : QRot{});
+            exact_unit<H16, TAB>(p, lds, wdim, sdim, u, g, wk, hist, tu, TAB ? rot : QRot{});
             continue;
         }
 
@@ -955,7 +960,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
         for (int x = 0; x < QB / 4; ++x) {
             char *rows4 = reinterpret_cast<char *>(p.out + (((int64_t)u * p.t + i0 + 4 * x) * p.hq + h) * kHeadDim);
-            if (wave_valid && i0 + 4 * x + (lane >> 4) < p.t)
+            if (wave_valid && i0 + 4 * x + (lane >> 4) < tu)
                 *reinterpret_cast<u32x4 *>(rows4 + olane) = orows[x];
         }
     } // work units
@@ -965,7 +970,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 
 hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
                                     const uint16_t *cache_v, const int32_t *positions,
-                                    const int32_t *lens, uint16_t *out, const PrefillShape &s,
+                                    const int32_t *lens, const int32_t *new_lens, uint16_t *out,
+                                    const PrefillShape &s,
                                     const RopeTable &tab, hipStream_t stream,
                                     hipEvent_t ev_before, hipEvent_t ev_after)
 {
@@ -977,6 +983,7 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
     p.cv = cache_v;
     p.pos = positions;
     p.lens = lens;
+    p.new_lens = new_lens;
     p.out = out;
     p.n = s.n;
     p.t = s.t;

@@ -207,8 +207,8 @@ __global__ void __launch_bounds__(256) append_kernel(uint16_t *__restrict__ cach
 __global__ void __launch_bounds__(256) rope_append_kernel(
     uint16_t *__restrict__ cache_k, uint16_t *__restrict__ cache_v,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ positions, const int32_t *__restrict__ lens, int max_len, int n,
-    int t, int hkv, int s_cap, RopeTable tab)
+    const int32_t *__restrict__ positions, const int32_t *__restrict__ lens,
+    const int32_t *__restrict__ new_lens, int max_len, int n, int t, int hkv, int s_cap, RopeTable tab)
 {
     const int64_t total = (int64_t)n * t * 16;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -221,6 +221,11 @@ __global__ void __launch_bounds__(256) rope_append_kernel(
     const int len = lens ? lens[u] : 0;
     if (len < 0 || len > max_len)
         return;
+    if (new_lens) {
+        const int tu = new_lens[u];
+        if (tu < 0 || tu > t || i >= tu)
+            return; // padding row, or an invalid count: nothing appended
+    }
     if (tab.half) {
         // chunks before `off` copy K; a first-half chunk rotates with its partner and
         // writes both; a second-half chunk only copies V
@@ -292,14 +297,14 @@ hipError_t launch_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k
 
 hipError_t launch_rope_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,
                               const uint16_t *v, const int32_t *positions, const int32_t *lens,
-                              int max_len, int n, int t, int hkv, int s_cap,
+                              const int32_t *new_lens, int max_len, int n, int t, int hkv, int s_cap,
                               const RopeTable &tab, hipStream_t stream)
 {
     const int64_t threads = (int64_t)n * t * 16;
     if (threads == 0)
         return hipSuccess;
     hipLaunchKernelGGL(rope_append_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
-                       cache_k, cache_v, k, v, positions, lens, max_len, n, t, hkv, s_cap, tab);
+                       cache_k, cache_v, k, v, positions, lens, new_lens, max_len, n, t, hkv, s_cap, tab);
     return hipGetLastError();
 }
 

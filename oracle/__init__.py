@@ -257,6 +257,32 @@ def prefill_kv(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, len
     return out, out64, k64
 
 
+def prefill_kv_varlen(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens, new_lens,
+                      scale: float, rp: RopeParams):
+    """prefill_kv over a batch whose unit u brings new_lens[u] new tokens (rows past it are
+    padding): unit u is prefill_kv of that unit alone on its first new_lens[u] rows ([Sophgo]
+    Listing 2 per sequence).  Caches are updated in place.  Returns (out bits, out fp64,
+    rotated k fp64) with NaN / 0 bits in the padding rows."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    pos, lens, nl = _i32(positions), _i32(lens), _i32(new_lens)
+    n, t = q.shape[:2]
+    out = np.zeros(q.shape, dtype=np.uint16)
+    out64 = np.full(q.shape, np.nan)
+    k64 = np.full(k.shape, np.nan)
+    for u in range(n):
+        tu = int(nl[u])
+        if not 0 <= tu <= t:
+            raise ValueError("oracle prefill_kv_varlen: new_lens out of range")
+        if tu == 0:
+            continue
+        ck, cv = np.ascontiguousarray(cache_k[u:u + 1]), np.ascontiguousarray(cache_v[u:u + 1])
+        o, o64, kk = prefill_kv(q[u:u + 1, :tu], k[u:u + 1, :tu], v[u:u + 1, :tu], pos[u:u + 1, :tu],
+                                ck, cv, lens[u:u + 1], scale, rp)
+        cache_k[u], cache_v[u] = ck[0], cv[0]
+        out[u, :tu], out64[u, :tu], k64[u, :tu] = o[0], o64[0], kk[0]
+    return out, out64, k64
+
+
 def prefill(q, k, v, positions, cache_k, cache_v, scale: float, rp: RopeParams):
     n = np.asarray(q).shape[0]
     return prefill_kv(q, k, v, positions, cache_k, cache_v, np.zeros(n, np.int32), scale, rp)

@@ -173,3 +173,39 @@ def test_kernel_f16_conversion_on_host(kv):
     assert np.array_equal(got, ref)
     nan = kv.f64_to_f16_bits(float("nan"))
     assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
+
+
+@pytest.mark.parametrize("field,value", [("pairing", 2), ("pairing", -1), ("inverse", 2)])
+def test_rotation_variant_validation(kv, field, value):
+    rp = kv.RopeParams.plain()
+    setattr(rp, field, value)
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ROPE
+
+
+@pytest.mark.parametrize("n_rot", [2, 16, 48, 100])
+def test_half_split_needs_a_multiple_of_32(kv, n_rot):
+    rp = kv.RopeParams.plain(n_rot=n_rot)
+    rp.pairing = 1
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ROPE
+
+
+def test_table_validation(kv):
+    rp = kv.RopeParams.plain()
+    rp.cos_table, rp.sin_table, rp.table_rows = A.value, None, 10
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ROPE          # one table without the other
+    rp.sin_table, rp.table_rows = A.value, 0
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ROPE          # no rows
+    rp.table_rows, rp.sin_table = 10, 0x10002
+    assert _prefill_kv(kv, rp=rp) == kv.KVROPE_ERR_ALIGN         # misaligned float table
+
+
+def test_varlen_host_validation(kv):
+    L = kv.lib()
+    rp = ctypes.byref(kv.RopeParams.plain())
+    args = [A, A, A, A, B, B, A, 10]
+    # NULL new-token counts, misaligned counts, zero-sized call
+    assert L.attn_prefill_kv_varlen(*args, None, B, 2, 4, 12, 2, 128, 20, 0.088, rp, None) == -1
+    assert L.attn_prefill_kv_varlen(*args, ctypes.c_void_p(0x10002), B, 2, 4, 12, 2, 128, 20, 0.088, rp,
+                                    None) == -5
+    assert L.attn_prefill_kv_varlen(*args, None, B, 0, 4, 12, 2, 128, 20, 0.088, rp, None) == 0
+    assert L.attn_prefill_kv_varlen(*args, A, B, 2, 4, 12, 2, 128, 13, 0.088, rp, None) == -4

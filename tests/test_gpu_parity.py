@@ -153,6 +153,46 @@ def test_prefill_kv_shapes(kv, n, t, hq, hkv, lens, rope):
     check_prefill(d, out, ref, lens, t, f"prefill_kv n{n} t{t} {hq}/{hkv} {lens}")
 
 
+@pytest.mark.parametrize("n,t,hq,hkv,lens,new,rope", [
+    (4, 70, 12, 2, [0, 100, 50, 7], [70, 1, 0, 33], W.PLAIN_128),
+    (3, 45, 32, 8, [300, 0, 37], [45, 17, 44], W.YARN_TAIL_64),
+    (2, 130, 8, 4, [0, 64], [129, 65], W.PLAIN_128),
+])
+def test_prefill_kv_varlen(kv, n, t, hq, hkv, lens, new, rope):
+    """Units with different new-token counts in one call: padding rows hold NaN in q, k, v
+    and must change nothing; their out rows keep the caller's values."""
+    cfg = custom(n, t, hq, hkv, max(lens) + t + 5, rope=rope, seed=350 + t)
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32))
+    for u in range(n):
+        for x in (inp.q, inp.k, inp.v):
+            x[u, new[u]:] = float("nan")
+    rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    rk0 = rk.copy()
+    ref_out, ref64, k64 = oracle.prefill_kv_varlen(bits(inp.q), bits(inp.k), bits(inp.v),
+                                                   inp.positions.numpy(), rk, rv, inp.lens.numpy(),
+                                                   np.asarray(new, np.int32), cfg.scale, ora_rope(rope))
+    d = to_dev(inp)
+    out = torch.full_like(d.q, 7.0)
+    kv.prefill_kv_varlen(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens,
+                         torch.tensor(new, dtype=torch.int32, device="cuda"), int(max(lens)),
+                         kv.RopeParams.from_fields(rope), scale=cfg.scale, out=out)
+    torch.cuda.synchronize()
+    got = bits(out)
+    seven = np.float16(7.0).view(np.uint16)
+    gk, gv = bits(d.cache_k), bits(d.cache_v)
+    assert np.array_equal(gv, rv), "varlen: V cache differs"
+    for u in range(n):
+        what = f"varlen n{n} t{t} {hq}/{hkv} unit {u} ({lens[u]} + {new[u]})"
+        if new[u]:
+            P.check_attention(got[u, :new[u]], ref64[u, :new[u]], what)
+        assert np.all(got[u, new[u]:] == seven), f"{what}: padding rows of out were written"
+        rows = slice(lens[u], lens[u] + new[u])
+        untouched = np.ones(gk.shape[2], bool)
+        untouched[rows] = False
+        assert np.array_equal(gk[u][:, untouched], rk0[u][:, untouched]), f"{what}: K rows changed"
+        P.check_k_rows(gk[u][:, rows], rk[u][:, rows], k64[u, :new[u]].transpose(1, 0, 2), what)
+
+
 def score_rise_log2(inp, ref, lens, rope, scale, hq, hkv):
     """Largest rise, over all rows, of a visible score above the row's max over keys
     0..63 (log2 units), from the oracle's rotated q and keys."""

@@ -239,3 +239,45 @@ def test_capacity_error_is_raised(ora):
     with pytest.raises(ValueError):
         ora.decode(q[:, 0].copy(), k[:, 0].copy(), v[:, 0].copy(), pos[:, 0].copy(), ck, cv,
                    [4], 0.3, ora.RopeParams.plain(n_rot=8))
+
+
+def test_varlen_with_full_counts_equals_batched_prefill_kv(ora):
+    rng = np.random.default_rng(36)
+    n, t, hq, hkv, d = 3, 9, 6, 2, 128
+    lens = [0, 5, 11]
+    q, k, v, pos, ck, cv = _case(rng, n, t, hq, hkv, d, lens, 24)
+    ck2, cv2 = ck.copy(), cv.copy()
+    out, out64, k64 = ora.prefill_kv(q, k, v, pos, ck, cv, lens, 0.09, ora.RopeParams.plain())
+    o2, o2_64, k2 = ora.prefill_kv_varlen(q, k, v, pos, ck2, cv2, lens, [t] * n, 0.09,
+                                          ora.RopeParams.plain())
+    assert np.array_equal(out, o2) and np.array_equal(out64, o2_64) and np.array_equal(k64, k2)
+    assert np.array_equal(ck, ck2) and np.array_equal(cv, cv2)
+
+
+def test_varlen_units_equal_their_own_successive_decodes(ora):
+    # each unit's valid rows against the decode loop (a separately written attention loop),
+    # one step per new token; padding rows hold NaN and change nothing; cache rows past each
+    # unit's new tokens stay as they were
+    rng = np.random.default_rng(37)
+    n, t, hq, hkv, d = 4, 8, 4, 2, 128
+    lens, new = [0, 6, 3, 9], [8, 1, 0, 5]
+    q, k, v, pos, ck, cv = _case(rng, n, t, hq, hkv, d, lens, 20)
+    nan16 = np.uint16(0x7e00)
+    for u in range(n):
+        q[u, new[u]:] = nan16
+        k[u, new[u]:] = nan16
+        v[u, new[u]:] = nan16
+    ck0, cv0 = ck.copy(), cv.copy()
+    rp = ora.RopeParams.yarn_tail()
+    out, out64, _ = ora.prefill_kv_varlen(q, k, v, pos, ck, cv, lens, new, 0.09, rp)
+    for u in range(n):
+        cku, cvu = ck0[u:u + 1].copy(), cv0[u:u + 1].copy()
+        for i in range(new[u]):
+            o, o64, _ = ora.decode(q[u:u + 1, i].copy(), k[u:u + 1, i].copy(), v[u:u + 1, i].copy(),
+                                   pos[u:u + 1, i].copy(), cku, cvu, np.array([lens[u] + i], np.int32),
+                                   0.09, rp)
+            np.testing.assert_allclose(out64[u, i], o64[0], rtol=1e-12, atol=1e-13)
+        assert np.array_equal(ck[u], cku[0]) and np.array_equal(cv[u], cvu[0])
+        assert np.isnan(out64[u, new[u]:]).all()
+        assert np.array_equal(ck[u][:, lens[u] + new[u]:], ck0[u][:, lens[u] + new[u]:])
+    assert np.all(np.isfinite(out64[0])) and np.all(np.isfinite(out64[1, :1]))
