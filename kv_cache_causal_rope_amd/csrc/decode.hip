@@ -386,7 +386,8 @@ int decode_chunk(int n, int hkv, int slices, int max_len)
     return 128;
 }
 
-int slice_width(int G) { return G >= 8 ? 8 : (G > 4 ? 8 : (G > 2 ? 4 : (G > 1 ? 2 : 1))); }
+// query heads per workgroup: the whole group up to 8 (no idle head slots in the VALU part)
+int slice_width(int G) { return G >= 8 ? 8 : G; }
 
 } // namespace
 
@@ -432,20 +433,11 @@ hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v
 
     if (ev_before)
         (void)hipEventRecord(ev_before, stream);
-    switch (gs) {
-    case 1:
-        hipLaunchKernelGGL(decode_split_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, p, tab);
-        break;
-    case 2:
-        hipLaunchKernelGGL(decode_split_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, p, tab);
-        break;
-    case 4:
-        hipLaunchKernelGGL(decode_split_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream, p, tab);
-        break;
-    default:
-        hipLaunchKernelGGL(decode_split_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, p, tab);
-        break;
-    }
+    using Kernel = void (*)(DecodeParams, RopeTable);
+    static const Kernel kernels[8] = {decode_split_kernel<1>, decode_split_kernel<2>, decode_split_kernel<3>,
+                                      decode_split_kernel<4>, decode_split_kernel<5>, decode_split_kernel<6>,
+                                      decode_split_kernel<7>, decode_split_kernel<8>};
+    hipLaunchKernelGGL(kernels[gs - 1], dim3((unsigned)blocks), dim3(256), 0, stream, p, tab);
     hipError_t err = hipGetLastError();
     if (ev_after)
         (void)hipEventRecord(ev_after, stream);
