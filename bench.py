@@ -207,6 +207,50 @@ def measured_mfma(kv):
                     f"v_mfma_f32_32x32x16_f16; clock from the shader and 100 MHz counters"}
 
 
+def bench_projections(kv, steps, warmup):
+    """The projections either side of attention on the 28-layer T=1024 Qwen-1.5B-style
+    prefill (hidden 1536, 12q/2kv x 128, one weight matrix per layer): the fused QKV
+    projection (k rotated and appended in its epilogue) and the output projection with the
+    residual, each as TFLOP/s over its 2 * tokens * N * K FLOPs."""
+    import torch
+    layers, t, hidden, hq, hkv, d = 28, 1024, 1536, 12, 2, 128
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rn = lambda *shape, s=1.0: (torch.randn(shape, generator=g, device="cuda") * s).half()
+    x = rn(layers, t, hidden)
+    w_qkv = rn(layers, (hq + 2 * hkv) * d, hidden, s=hidden ** -0.5)
+    w_o = rn(layers, hidden, hq * d, s=(hq * d) ** -0.5)
+    ck = torch.zeros(layers, hkv, t, d, dtype=torch.float16, device="cuda")
+    cv = torch.zeros_like(ck)
+    pos = torch.arange(t, dtype=torch.int32, device="cuda").repeat(layers, 1).contiguous()
+    lens = torch.zeros(layers, dtype=torch.int32, device="cuda")
+    q = torch.empty(layers, t, hq, d, dtype=torch.float16, device="cuda")
+    attn = rn(layers, t, hq, d)
+    out = torch.empty_like(x)
+    rp = kv.RopeParams.plain()
+    res = {}
+    for name, call, flops in [
+            ("qkv_project", lambda: kv.qkv_project(x, w_qkv, pos, ck, cv, lens, 0, rp, hq, hkv, q_out=q),
+             2.0 * layers * t * (hq + 2 * hkv) * d * hidden),
+            ("out_project", lambda: kv.out_project(attn, w_o, x, out=out), 2.0 * layers * t * hidden * hq * d)]:
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = make_events(2)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "us": round(ms * 1e3, 1), "flops": flops,
+                     "frac_of_f16_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+    del x, w_qkv, w_o, ck, cv, q, attn, out
+    torch.cuda.empty_cache()
+    res["workload"] = "28 layers x T=1024, hidden 1536, 12q/2kv x 128, per-layer weights"
+    return res
+
+
 def cpu_baseline(W, name, units):
     """The oracle (untuned, fp64, OpenMP) on `units` layers of the prefill workload."""
     import numpy as np
@@ -239,6 +283,7 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-projections", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -296,6 +341,13 @@ def main():
                                                       "same chunking",
                                               "kernel_frac": round(kgbs / ceil_gbs, 4)}})
 
+    proj = None
+    if not args.no_projections:
+        proj = bench_projections(kv, max(5, args.steps // 2), min(args.warmup, 3))
+        log(f"[bench] projections: QKV {proj['qkv_project']['tflops']:.0f} TFLOP/s "
+            f"({proj['qkv_project']['us']:.1f} us), out {proj['out_project']['tflops']:.0f} TFLOP/s "
+            f"({proj['out_project']['us']:.1f} us)")
+
     ceilings = measured_mfma(kv)
     log(f"[bench] f16 MFMA microbenchmark: {ceilings['mfma_f16_tflops']:.0f} TFLOP/s at "
         f"{ceilings['sclk_mhz']:.0f} MHz shader clock")
@@ -326,6 +378,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": traffic("prefill_attn", cfg.name)},
         "decode": decode,
+        "projections": proj,
         "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }

@@ -175,6 +175,48 @@ int attn_decode(const void *q, const void *k, const void *v, const int32_t *posi
                 const kvrope_rope_params *rp, void *workspace, size_t ws_bytes,
                 void *stream);
 
+/* ---- The projections either side of attention ([Sophgo] Listings 1-2: q, k, v =
+ * MatMul(x, w_q / w_k / w_v), Rope on q and k, Concat into the cache; h = Add(input,
+ * MatMul(attn, w_o))), on f16 MFMA with fp32 accumulation.  Weights are stored one row per
+ * output feature ([out_features, in_features], the transpose of the listings' w), so
+ * y = x . w^T.  w_per_unit = 0: one weight matrix for all n units; 1: n matrices back to
+ * back (e.g. one per layer when the units are layers).
+ *
+ * attn_qkv_project -- the QKV projection with the rotary embedding of k and the cache
+ * append as its epilogue.
+ *   x       device, f16 [n, t, hidden]; hidden a multiple of 64
+ *   w_qkv   device, f16 [(w_per_unit ? n : 1), (hq + 2 hkv) * d, hidden]: rows 0 .. hq d - 1
+ *           project q (head h = rows h d .. h d + d - 1), then hkv * d rows for k, then v
+ *   q       device, f16 [n, t, hq, d] out: the projected q, rounded to f16, NOT rotated (the
+ *           attention entry points rotate q themselves)
+ *   k, v    never written to memory: the projected k (rounded to f16) is rotated at
+ *           positions[u][i] exactly as attn_rope_apply rotates (fp64, rounded once) and
+ *           written with v (rounded to f16) to cache rows lens[u] + i, i < t
+ *   lens, max_len, s_cap, positions, rp: as for attn_prefill_kv (lens may be NULL: all 0)
+ * Each projected value is the f16 rounding of an fp32-accumulated dot product, so it may
+ * differ by one f16 ulp from the rounding of the exact product where the two straddle a
+ * rounding boundary.
+ *
+ * attn_out_project -- out = attn . w_o^T + residual, rounded once to f16.
+ *   attn      device, f16 [n, t, hq * d]  (the attention output, [n, t, hq, d])
+ *   w_o       device, f16 [(w_per_unit ? n : 1), hidden, hq * d]; hidden a multiple of 128
+ *   residual  device, f16 [n, t, hidden];  out  device, f16 [n, t, hidden] (may alias
+ *             residual)
+ * Both are asynchronous on `stream` and return KVROPE_OK, KVROPE_ERR_SHAPE, KVROPE_ERR_NULL,
+ * KVROPE_ERR_ALIGN, KVROPE_ERR_CAPACITY / KVROPE_ERR_ROPE (qkv) or KVROPE_ERR_HIP. */
+/* attn_prefill_kv_cached -- attn_prefill_kv whose new k, v rows are already in the caches
+ * (written by attn_qkv_project): rows [hist_lens[u], hist_lens[u] + t) of each cache hold
+ * the rotated k and the v of the t new tokens; the caches are only read.  q is the
+ * unrotated query (rotated here at `positions`); everything else as attn_prefill_kv. */
+int attn_prefill_kv_cached(const void *q, const int32_t *positions, const void *cache_k, const void *cache_v,
+                           const int32_t *hist_lens, int max_hist, void *out, int n, int t, int hq, int hkv,
+                           int d, int s_cap, double scale, const kvrope_rope_params *rp, void *stream);
+int attn_qkv_project(const void *x, const void *w_qkv, int w_per_unit, const int32_t *positions, void *q,
+                     void *cache_k, void *cache_v, const int32_t *lens, int max_len, int n, int t, int hidden,
+                     int hq, int hkv, int d, int s_cap, const kvrope_rope_params *rp, void *stream);
+int attn_out_project(const void *attn, const void *w_o, int w_per_unit, const void *residual, void *out, int n,
+                     int t, int hq, int d, int hidden, void *stream);
+
 #define KVROPE_OP_DECODE 1
 
 /* Bytes of device workspace the operation needs (0 for operations that need none). */

@@ -39,7 +39,8 @@ KVROPE_OP_DECODE = 1
 EXPORTS = ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
            "attn_prefill_kv_varlen", "attn_decode", "kvrope_workspace_size", "kvrope_status_string",
            "kvrope_last_hip_error", "kvrope_set_profile_events", "kvrope_f64_to_f16",
-           "kvrope_probe_stream", "kvrope_probe_mfma"]
+           "kvrope_probe_stream", "kvrope_probe_mfma", "attn_qkv_project", "attn_out_project",
+           "attn_prefill_kv_cached"]
 
 
 class KVRopeError(RuntimeError):
@@ -146,9 +147,12 @@ def lib() -> ctypes.CDLL:
     L.kvrope_f64_to_f16.restype = ctypes.c_uint16
     L.kvrope_probe_stream.argtypes = [_P, _P, _P] + [_I] * 6 + [_P, _P]
     L.kvrope_probe_mfma.argtypes = [_I, _I, _P, _P]
+    L.attn_qkv_project.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P] + [_I] * 8 + [rp, _P]
+    L.attn_out_project.argtypes = [_P, _P, _I, _P, _P] + [_I] * 5 + [_P]
+    L.attn_prefill_kv_cached.argtypes = [_P] * 5 + [_I, _P] + [_I] * 6 + [ctypes.c_double, rp, _P]
     for rtn in ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
                 "attn_prefill_kv_varlen", "attn_decode", "kvrope_set_profile_events", "kvrope_probe_stream",
-                "kvrope_probe_mfma"]:
+                "kvrope_probe_mfma", "attn_qkv_project", "attn_out_project", "attn_prefill_kv_cached"]:
         getattr(L, rtn).restype = _I
     _lib = L
     return L
@@ -313,6 +317,83 @@ def prefill_kv_varlen(q, k, v, positions, cache_k, cache_v, hist_lens, new_lens,
                                         _ptr(cache_v), _ptr(hist_lens), int(max_hist), _ptr(new_lens),
                                         _ptr(out), n, t, hq, hkv, d, s_cap, float(scale),
                                         ctypes.byref(rope), _stream(stream)))
+    return out
+
+
+def _weights(w: torch.Tensor, n: int, rows: int, cols: int, name: str) -> int:
+    """w [rows, cols] (shared) or [n, rows, cols] (one per unit); returns w_per_unit."""
+    per_unit = 1 if w.dim() == 3 else 0
+    _f16(name, w, (n, rows, cols) if per_unit else (rows, cols))
+    return per_unit
+
+
+def qkv_project(x, w_qkv, positions, cache_k, cache_v, lens, max_len: int, rope: RopeParams, hq: int,
+                hkv: int, q_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Fused QKV projection: returns q [n, t, hq, 128] (unrotated); k (rotated) and v go
+    to cache rows lens[u] + i.  x [n, t, hidden]; w_qkv [(hq + 2 hkv) * 128, hidden] or one
+    such matrix per unit [n, ...]."""
+    if x.dim() != 3:
+        raise ValueError("x must be [n, t, hidden]")
+    n, t, hidden = x.shape
+    d = 128
+    _f16("x", x, (n, t, hidden))
+    per_unit = _weights(w_qkv, n, (hq + 2 * hkv) * d, hidden, "w_qkv")
+    s_cap = cache_k.shape[2]
+    _f16("cache_k", cache_k, (n, hkv, s_cap, d))
+    _f16("cache_v", cache_v, (n, hkv, s_cap, d))
+    _i32("positions", positions, (n, t))
+    if lens is not None:
+        _i32("lens", lens, (n,))
+    if q_out is None:
+        q_out = torch.empty((n, t, hq, d), dtype=torch.float16, device=x.device)
+    _f16("q_out", q_out, (n, t, hq, d))
+    _check(lib().attn_qkv_project(_ptr(x), _ptr(w_qkv), per_unit, _ptr(positions), _ptr(q_out),
+                                  _ptr(cache_k), _ptr(cache_v), _ptr(lens) if lens is not None else None,
+                                  int(max_len), n, t, hidden, hq, hkv, d, s_cap, ctypes.byref(rope),
+                                  _stream(stream)))
+    return q_out
+
+
+def prefill_kv_cached(q, positions, cache_k, cache_v, hist_lens, max_hist: int, rope: RopeParams,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """prefill_kv over caches that already hold the new rows (from qkv_project)."""
+    n, t, hq, d = q.shape
+    _f16("q", q, (n, t, hq, d))
+    hkv, s_cap = cache_k.shape[1], cache_k.shape[2]
+    _f16("cache_k", cache_k, (n, hkv, s_cap, d))
+    _f16("cache_v", cache_v, (n, hkv, s_cap, d))
+    _i32("positions", positions, (n, t))
+    if hist_lens is not None:
+        _i32("hist_lens", hist_lens, (n,))
+    if out is None:
+        out = torch.empty_like(q)
+    _f16("out", out, q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _check(lib().attn_prefill_kv_cached(_ptr(q), _ptr(positions), _ptr(cache_k), _ptr(cache_v),
+                                        _ptr(hist_lens) if hist_lens is not None else None, int(max_hist),
+                                        _ptr(out), n, t, hq, hkv, d, s_cap, float(scale), ctypes.byref(rope),
+                                        _stream(stream)))
+    return out
+
+
+def out_project(attn, w_o, residual, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out = attn . w_o^T + residual.  attn [n, t, hq, 128]; w_o [hidden, hq * 128] or
+    [n, hidden, hq * 128]; residual [n, t, hidden]."""
+    if attn.dim() != 4:
+        raise ValueError("attn must be [n, t, hq, 128]")
+    n, t, hq, d = attn.shape
+    _f16("attn", attn, (n, t, hq, d))
+    if residual.dim() != 3:
+        raise ValueError("residual must be [n, t, hidden]")
+    hidden = residual.shape[2]
+    _f16("residual", residual, (n, t, hidden))
+    per_unit = _weights(w_o, n, hidden, hq * d, "w_o")
+    if out is None:
+        out = torch.empty_like(residual)
+    _f16("out", out, (n, t, hidden))
+    _check(lib().attn_out_project(_ptr(attn), _ptr(w_o), per_unit, _ptr(residual), _ptr(out), n, t, hq, d,
+                                  hidden, _stream(stream)))
     return out
 
 

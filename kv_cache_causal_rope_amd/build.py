@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libkvrope.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("KVROPE_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "rope_append.hip", "prefill.hip", "decode.hip", "probes.hip"]
+SOURCES = ["api.hip", "rope_append.hip", "prefill.hip", "decode.hip", "probes.hip", "gemm.hip"]
 
 # Packed fp32 instructions are switched off for all device code (the compiler would
 # otherwise form v_pk_* from ordinary float code).

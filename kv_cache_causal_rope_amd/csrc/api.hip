@@ -320,4 +320,86 @@ int attn_decode(const void *q, const void *k, const void *v, const int32_t *posi
                                             static_cast<hipStream_t>(stream), eb, ea));
 }
 
+int attn_prefill_kv_cached(const void *q, const int32_t *positions, const void *cache_k, const void *cache_v,
+                           const int32_t *hist_lens, int max_hist, void *out, int n, int t, int hq, int hkv,
+                           int d, int s_cap, double scale, const kvrope_rope_params *rp, void *stream)
+{
+    if (n < 0 || t < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || d != kvrope::kHeadDim || s_cap < 1)
+        return KVROPE_ERR_SHAPE;
+    int st = check_rope(rp, d);
+    if (st)
+        return st;
+    if (!(isfinite(scale) && scale > 0.0))
+        return KVROPE_ERR_SCALE;
+    if (max_hist < 0 || (int64_t)max_hist + t > s_cap)
+        return KVROPE_ERR_CAPACITY;
+    if ((int64_t)n * t == 0)
+        return KVROPE_OK;
+    if (!q || !positions || !cache_k || !cache_v || !out)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) || !aligned16(out) || !aligned4(positions) ||
+        (hist_lens && !aligned4(hist_lens)))
+        return KVROPE_ERR_ALIGN;
+    if ((int64_t)n * hkv * (hq / hkv) * ((t + 31) / 32) > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    const kvrope::RopeTable tab = rope_table(*rp, d);
+    hipEvent_t eb, ea;
+    take_profile_events(&eb, &ea);
+    kvrope::PrefillShape ps{n, t, hq, hkv, s_cap, max_hist, (float)scale};
+    return hip_status(kvrope::launch_prefill_attention(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(cache_k),
+        static_cast<const uint16_t *>(cache_v), positions, hist_lens, nullptr, static_cast<uint16_t *>(out), ps,
+        tab, static_cast<hipStream_t>(stream), eb, ea));
+}
+
+int attn_qkv_project(const void *x, const void *w_qkv, int w_per_unit, const int32_t *positions, void *q,
+                     void *cache_k, void *cache_v, const int32_t *lens, int max_len, int n, int t, int hidden,
+                     int hq, int hkv, int d, int s_cap, const kvrope_rope_params *rp, void *stream)
+{
+    if (n < 0 || t < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || d != kvrope::kHeadDim || s_cap < 1 ||
+        hidden < 64 || hidden % 64 != 0 || (w_per_unit != 0 && w_per_unit != 1))
+        return KVROPE_ERR_SHAPE;
+    int st = check_rope(rp, d);
+    if (st)
+        return st;
+    if (max_len < 0 || (int64_t)max_len + t > s_cap)
+        return KVROPE_ERR_CAPACITY;
+    if ((int64_t)n * t == 0)
+        return KVROPE_OK;
+    if (!x || !w_qkv || !positions || !q || !cache_k || !cache_v)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(cache_k) || !aligned16(cache_v) ||
+        !aligned4(positions) || (lens && !aligned4(lens)))
+        return KVROPE_ERR_ALIGN;
+    const int64_t nout = (int64_t)(hq + 2 * hkv) * d;
+    if ((int64_t)n * ((t + 127) / 128) * (nout / 128) > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    const kvrope::RopeTable tab = rope_table(*rp, d);
+    return hip_status(kvrope::launch_qkv_projection(
+        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_qkv), w_per_unit ? nout * hidden : 0,
+        positions, static_cast<uint16_t *>(q), static_cast<uint16_t *>(cache_k), static_cast<uint16_t *>(cache_v),
+        lens, max_len, n, t, hidden, hq, hkv, s_cap, tab, static_cast<hipStream_t>(stream)));
+}
+
+int attn_out_project(const void *attn, const void *w_o, int w_per_unit, const void *residual, void *out, int n,
+                     int t, int hq, int d, int hidden, void *stream)
+{
+    if (n < 0 || t < 0 || hq < 1 || d != kvrope::kHeadDim || hidden < 128 || hidden % 128 != 0 ||
+        (w_per_unit != 0 && w_per_unit != 1))
+        return KVROPE_ERR_SHAPE;
+    if ((int64_t)n * t == 0)
+        return KVROPE_OK;
+    if (!attn || !w_o || !residual || !out)
+        return KVROPE_ERR_NULL;
+    if (!aligned16(attn) || !aligned16(w_o) || !aligned16(residual) || !aligned16(out))
+        return KVROPE_ERR_ALIGN;
+    const int in_features = hq * d;
+    if ((int64_t)n * ((t + 127) / 128) * (hidden / 128) > kMaxGrid)
+        return KVROPE_ERR_SHAPE;
+    return hip_status(kvrope::launch_out_projection(
+        static_cast<const uint16_t *>(attn), static_cast<const uint16_t *>(w_o),
+        w_per_unit ? (int64_t)hidden * in_features : 0, static_cast<const uint16_t *>(residual),
+        static_cast<uint16_t *>(out), n, t, in_features, hidden, static_cast<hipStream_t>(stream)));
+}
+
 } // extern "C"

@@ -37,6 +37,17 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
                                     const RopeTable &tab, hipStream_t stream,
                                     hipEvent_t ev_before, hipEvent_t ev_after);
 
+// Fused QKV projection (C = x . w^T, w [(hq + 2 hkv) * 128, hidden] per unit or shared):
+// q heads written to q, k heads rotated and v heads copied into cache rows lens[u] + i.
+hipError_t launch_qkv_projection(const uint16_t *x, const uint16_t *w, int64_t w_stride, const int32_t *positions,
+                                 uint16_t *q, uint16_t *cache_k, uint16_t *cache_v, const int32_t *lens,
+                                 int max_len, int n, int t, int hidden, int hq, int hkv, int s_cap,
+                                 const RopeTable &tab, hipStream_t stream);
+
+// Output projection: out = attn . w^T + residual, w [hidden, in_features] per unit or shared.
+hipError_t launch_out_projection(const uint16_t *attn, const uint16_t *w, int64_t w_stride, const uint16_t *residual,
+                                 uint16_t *out, int n, int t, int in_features, int hidden, hipStream_t stream);
+
 struct DecodeShape {
     int n, hq, hkv, s_cap, max_len;
     float scale;

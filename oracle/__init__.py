@@ -216,6 +216,49 @@ def rope(x, positions, rp: RopeParams):
     return out, out64
 
 
+# ---------------------------------------------------------------- projections
+def project(a, w) -> tuple:
+    """y = a . w^T ([Sophgo] Listings 1-2: MatMul(x, w) with w stored one row per output
+    feature).  a [..., K], w [N, K] f16 bits.  Every product of two f16 values is exact in
+    fp64 and the sum of K of them keeps ~53 bits, so the result is the exact dot product to
+    within far less than an f16 ulp.  Returns (fp64 [..., N], RNE f16 bits)."""
+    a64 = f16_to_f64(a)
+    w64 = f16_to_f64(w)
+    y = a64 @ w64.T
+    return y, f64_to_f16(y)
+
+
+def qkv_project(x, w_qkv, hq: int, hkv: int, d: int = 128):
+    """x [n, t, hidden], w_qkv [(hq + 2 hkv) d, hidden] (or one per unit: [n, ...]) f16 bits.
+    Returns the f16 q [n,t,hq,d], k [n,t,hkv,d], v [n,t,hkv,d] of the projection."""
+    x, w = _u16(x), _u16(w_qkv)
+    n, t, _ = x.shape
+    if w.ndim == 2:
+        _, y = project(x.reshape(n * t, -1), w)
+        y = y.reshape(n, t, -1)
+    else:
+        y = np.stack([project(x[u], w[u])[1] for u in range(n)])
+    q = y[..., : hq * d].reshape(n, t, hq, d)
+    k = y[..., hq * d: (hq + hkv) * d].reshape(n, t, hkv, d)
+    v = y[..., (hq + hkv) * d:].reshape(n, t, hkv, d)
+    return np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def out_project(attn, w_o, residual):
+    """out = attn . w_o^T + residual ([Sophgo] Listings 1-2: Add(input, MatMul(attn, w_o))),
+    rounded once to f16.  attn [n, t, F], w_o [hidden, F] (or [n, hidden, F]), residual
+    [n, t, hidden] f16 bits.  Returns (fp64, f16 bits)."""
+    attn, w, res = _u16(attn), _u16(w_o), _u16(residual)
+    n, t = attn.shape[:2]
+    a = attn.reshape(n, t, -1)
+    if w.ndim == 2:
+        y = project(a.reshape(n * t, -1), w)[0].reshape(n, t, -1)
+    else:
+        y = np.stack([project(a[u], w[u])[0] for u in range(n)])
+    y = y + f16_to_f64(res)
+    return y, f64_to_f16(y)
+
+
 # ---------------------------------------------------------------- cache append
 def append(cache_k: np.ndarray, cache_v: np.ndarray, k, v, lens) -> None:
     """In place: rows [lens[n], lens[n]+t) of each cache get k / v (bit copy)."""
