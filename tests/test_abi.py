@@ -209,3 +209,31 @@ def test_varlen_host_validation(kv):
                                     None) == -5
     assert L.attn_prefill_kv_varlen(*args, None, B, 0, 4, 12, 2, 128, 20, 0.088, rp, None) == 0
     assert L.attn_prefill_kv_varlen(*args, A, B, 2, 4, 12, 2, 128, 13, 0.088, rp, None) == -4
+
+
+def test_projection_host_validation(kv):
+    L = kv.lib()
+    rp = ctypes.byref(kv.RopeParams.plain())
+    # x, w, w_per_unit, pos, q, ck, cv, lens, max_len, n, t, hidden, hq, hkv, d, s_cap
+    ok = [A, A, 0, A, B, B, B, A, 4, 2, 8, 256, 12, 2, 128, 16]
+    def qkv(**over):
+        args = list(ok)
+        for i, val in over.items():
+            args[int(i[1:])] = val
+        return L.attn_qkv_project(*args, rp, None)
+    assert qkv(a11=100) == -2          # hidden not a multiple of 64
+    assert qkv(a2=2) == -2             # w_per_unit not 0/1
+    assert qkv(a14=64) == -2           # head dim
+    assert qkv(a0=None) == -1
+    assert qkv(a4=UNALIGNED) == -5
+    assert qkv(a15=11) == -4           # max_len + t > s_cap
+    assert qkv(a9=0) == 0              # nothing to do
+    # attn, w_o, w_per_unit, residual, out, n, t, hq, d, hidden
+    assert L.attn_out_project(A, A, 0, A, B, 2, 8, 12, 128, 100, None) == -2   # hidden % 128
+    assert L.attn_out_project(A, None, 0, A, B, 2, 8, 12, 128, 256, None) == -1
+    assert L.attn_out_project(A, A, 0, UNALIGNED, B, 2, 8, 12, 128, 256, None) == -5
+    assert L.attn_out_project(A, A, 0, A, B, 0, 8, 12, 128, 256, None) == 0
+    # q, pos, ck, cv, hist, max_hist, out, n, t, hq, hkv, d, s_cap, scale
+    assert L.attn_prefill_kv_cached(A, A, B, B, A, 4, B, 2, 8, 12, 2, 128, 11, 0.1, rp, None) == -4
+    assert L.attn_prefill_kv_cached(A, A, B, B, A, 4, B, 2, 8, 12, 2, 128, 16, 0.0, rp, None) == -7
+    assert L.attn_prefill_kv_cached(None, A, B, B, A, 4, B, 2, 8, 12, 2, 128, 16, 0.1, rp, None) == -1
