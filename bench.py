@@ -37,21 +37,24 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes of this script,
 # scaled by what the same counters read for a plain 1 GiB device copy (FETCH_SIZE x 2.0,
 # WRITE_SIZE x 1.0; profiles/hbm_traffic_counters.md).  `src` is the sha256 of the kernel
-# source and the shared device header at measurement time: once either changes, the
+# source and the shared device headers at measurement time: once any changes, the
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 267.086e6,
-        "src": ("4bb063631012e789141dc4ccfe58075e3f27c878de7dfdadd951061f9ed0eb54",
-                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f")},
+        "bytes": 266.964e6,
+        "src": ("c2ae1db4642f2d4ce157e83962dfe8d276e17375e4482f3e1db97ffa6c7a22ea",
+                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
+                "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
     "decode_split:qwen1p5b_decode_l4096_b32": {
-        "bytes": 2.83173e9,
-        "src": ("4a1e5b7edde7d82f6a74f4594169dd786604aa0228b28f37a59698b44ab43b7f",
-                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f")},
+        "bytes": 2.83175e9,
+        "src": ("539ae65605d09c5c2f1885ac90290ee409e898a4480e07279581126dde283480",
+                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
+                "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
     "decode_split:yarn_decode_l32k_b64": {
-        "bytes": 23.03665e9,
-        "src": ("4a1e5b7edde7d82f6a74f4594169dd786604aa0228b28f37a59698b44ab43b7f",
-                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f")},
+        "bytes": 23.03663e9,
+        "src": ("539ae65605d09c5c2f1885ac90290ee409e898a4480e07279581126dde283480",
+                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
+                "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
 }
 KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_split": "decode.hip"}
 
@@ -83,7 +86,7 @@ def traffic(kernel, workload):
         return None
     csrc = os.path.join(ROOT, "kv_cache_causal_rope_amd", "csrc")
     now = tuple(hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
-                for f in (KERNEL_SOURCES[kernel], "device_common.h"))
+                for f in (KERNEL_SOURCES[kernel], "device_common.h", "rope_device.h"))
     return rec["bytes"] if now == rec["src"] else None
 
 
