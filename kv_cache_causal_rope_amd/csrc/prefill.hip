@@ -44,12 +44,10 @@
 //           hit distinct banks.  It goes from HBM/L2 straight into LDS
 //           (global_load_lds_dwordx4: lane L of a wave's load lands at byte 16 L of a
 //           1 KB block; the swizzle picks which global chunk each lane fetches).
-//   V tile: pre-transposed for the PV A-operand, [4 groups of 16 keys][2 lane halves]
-//           [128 dims][8 keys]: the 8 keys of (group, half) are the ones that half's
-//           lanes contribute to one 16-key MFMA step, so each A operand is a single
-//           16-byte read; the dim index is xor-swizzled inside groups of 8 to spread the
-//           transposing writes.  V rows are staged through registers (2 rows x 16 B per
-//           thread) one phase pair before they are written.
+//   V tile: row-major like K, loaded the same way (HBM/L2 straight into LDS), chunk
+//           index xor-swizzled by 4 (key % 4).  The PV A-operand (8 keys of one dim per
+//           lane) comes out of two transposing reads (ds_read_b64_tr_b16, 4 keys each), so
+//           V never passes through registers and the softmax phase issues no LDS stores.
 // Tile loads use a wave-uniform tile base address plus per-lane 32-bit offsets fixed for
 // the whole kernel; only a workgroup's last, partial tile clamps rows to the last key.
 // Persistent grid: one workgroup per compute unit loops over the work units (8 items
@@ -129,6 +127,20 @@ __device__ inline void wg_barrier_reads_in_flight()
 }
 
 __device__ inline int kswz(int key) { return key & 15; }
+// V rows: 16-byte chunk index xor 4 (key % 4), so the four rows one transposing read
+// covers per lane half sit on distinct banks
+__device__ inline int vswz(int key) { return 4 * (key & 3); }
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at LDS byte offset `off`: within each 16-lane group, lane i receives
+// 16-bit element i % 4 of the 8 bytes that lane 4 j + i / 4 addresses, as its element j.
+__device__ inline u32x2 lds_read_tr16(const char *lds, uint32_t off)
+{
+    const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v *)(lds + off));
+    return __builtin_bit_cast(u32x2, v);
+}
 
 __device__ inline uint32_t lds_offset(const void *p)
 {
@@ -142,6 +154,26 @@ __device__ inline int krow(int wave, int lane, int i) { return 8 * wave + 4 * i 
 __device__ inline uint32_t koffset(int row, int lane)
 {
     return (uint32_t)(row * ROWB + (((lane & 15) ^ kswz(row)) << 4));
+}
+
+// Per-lane base of the V^T operand reads (stage 0).  For key step x and dim block db the
+// lane's two transposing reads (keys 16 x + 4 hh + 0..3, then + 8..11) sit at
+// (base ^ 64 db) + 4 KB x (+ 2 KB): in its 16-lane group (gq = lane / 16; gq % 2 picks
+// which 16 dims of the block), lane 4 j + r addresses key row 16 x + 4 hh + j, dims
+// 32 db + 16 (gq % 2) + 4 r .. + 3, i.e. chunk 4 db + 2 (gq % 2) + r / 2 swizzled to
+// 4 (db ^ j) + 2 (gq % 2) + r / 2.
+__device__ inline uint32_t vt_base(int lane)
+{
+    const int hh = lane >> 5, j = (lane >> 2) & 3, r = lane & 3;
+    return (uint32_t)(VREG_B + (4 * hh + j) * ROWB + 64 * j + 32 * ((lane >> 4) & 1) + 8 * r);
+}
+
+// V^T operand of key step x, dim block db from the stage at byte offset so
+__device__ inline half8 read_vt(const char *lds, uint32_t vb, int so, int x, int db)
+{
+    const uint32_t a = (vb ^ (uint32_t)(64 * db)) + (uint32_t)so + (uint32_t)(x * 16 * ROWB);
+    const u32x2 lo = lds_read_tr16(lds, a), hi = lds_read_tr16(lds, a + 8 * ROWB);
+    return __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
 // A wave-uniform pointer held in vector registers (e.g. an argument of a
@@ -170,63 +202,6 @@ __device__ inline void dma_k(const char *tile, const uint32_t (&off)[2], uint32_
     }
 }
 
-// V staging: thread tid owns lane half hh = (tid >> 6) & 1 of key group grp = tid >> 7,
-// the 8-dim chunk m = (tid >> 2) & 15 and the key pair kq = tid & 3 of that half's list
-// (keys 16 grp + 4 hh + {0, 1, 2, 3, 8, 9, 10, 11}).
-struct VRegs {
-    u32x4 a, b;
-};
-
-__device__ inline int vkey(int tid, int which)
-{
-    const int kq = tid & 3, hh = (tid >> 6) & 1, grp = tid >> 7;
-    const int pos = 2 * kq + which;
-    return 16 * grp + 4 * hh + (pos < 4 ? pos : pos + 4);
-}
-
-__device__ inline uint32_t voffset(int key, int tid) { return (uint32_t)(key * ROWB + 16 * ((tid >> 2) & 15)); }
-
-__device__ inline void load_v(VRegs &r, const char *tile, const uint32_t (&off)[2])
-{
-    r.a = *reinterpret_cast<const u32x4 *>(tile + off[0]);
-    r.b = *reinterpret_cast<const u32x4 *>(tile + off[1]);
-}
-
-__device__ inline int vpos(int dim) { return dim ^ ((dim >> 3) & 7); }
-
-// LDS byte offset (stage 0) where thread tid writes dim 8m + e of its two keys.
-__device__ inline uint32_t vstore_offset(int tid, int e)
-{
-    const int kq = tid & 3, m = (tid >> 2) & 15, hh = (tid >> 6) & 1, grp = tid >> 7;
-    return (uint32_t)(VREG_B + ((grp * 2 + hh) * kHeadDim + vpos(8 * m + e)) * 16 + 4 * kq);
-}
-
-// Transposing write of the staged rows into the V region of stage STG (an immediate
-// offset from the thread's eight stage-0 addresses): dim 8m + e of the first key goes to
-// the low half of its word, of the second key to the high half.  The 16-bit stores take
-// either half of a register directly, so the transpose costs no vector ALU work (as
-// plain C++ the compiler would merge each pair into one 32-bit store behind a v_perm).
-// They are inline asm: the barrier that publishes the stage waits for them (lgkmcnt),
-// and LDS operations complete in order, so later compiler-counted waits stay correct.
-template <int STG>
-__device__ inline void store_v(const VRegs &r, char *lds, const uint32_t (&vst)[8])
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t addr = lds_offset(lds) + vst[e];
-        const uint32_t x = r.a[e >> 1], y = r.b[e >> 1];
-        if (e & 1)
-            asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2\n\tds_write_b16_d16_hi %0, %3 offset:%4"
-                         :
-                         : "v"(addr), "v"(x), "i"(STG * TILE_B), "v"(y), "i"(STG * TILE_B + 2)
-                         : "memory");
-        else
-            asm volatile("ds_write_b16 %0, %1 offset:%2\n\tds_write_b16 %0, %3 offset:%4"
-                         :
-                         : "v"(addr), "v"(x), "i"(STG * TILE_B), "v"(y), "i"(STG * TILE_B + 2)
-                         : "memory");
-    }
-}
 
 // Factors (c, s) of slot dp at position qpos, times the slot's output scale sdim[dp]:
 // fp32 trig of the fp64-reduced angle (signed revolutions wdim[dp] per position, negative
@@ -413,10 +388,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     half8 qop[8];
     rotate_q_t<H16, TAB>(qop, qin, p.pos[(int64_t)u * p.t + iq], hh, wdim, sdim, rot);
 
-    uint32_t vst[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        vst[e] = vstore_offset(tid, e);
+    const uint32_t vb = vt_base(lane);
     floatx16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -424,19 +396,18 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     float m_run = -INFINITY, l_run = 0.f;
     for (int j = 0; j < ntiles; ++j) {
         const int kb = j * KT;
-        // K rows (clamped past kend) straight into stage 0, V rows through registers
+        // K and V rows (clamped past kend) straight into stage 0
         uint32_t ko[2], vo[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int row = krow(wave, lane, r);
             ko[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
-            vo[r] = voffset(min(vkey(tid, r), klast - kb), tid);
+            vo[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ vswz(row)) << 4));
         }
-        dma_k(uniform_ptr(kbase + (int64_t)kb * ROWB), ko, __builtin_amdgcn_readfirstlane(lds_offset(lds)), wave);
-        VRegs vr;
-        load_v(vr, vbase + (int64_t)__builtin_amdgcn_readfirstlane(kb) * ROWB, vo);
+        const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+        dma_k(uniform_ptr(kbase + (int64_t)kb * ROWB), ko, lds0, wave);
+        dma_k(uniform_ptr(vbase + (int64_t)kb * ROWB), vo, lds0 + VREG_B, wave);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        store_v<0>(vr, lds, vst);
         wg_barrier();
 
         floatx16 sacc[2] = {floatx16{0.f}, floatx16{0.f}};
@@ -482,8 +453,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int db = x & 3;
-            const half8 a = *reinterpret_cast<const half8 *>(lds + VREG_B + hh * kHeadDim * 16 +
-                                                             vpos(32 * db + c) * 16 + (x >> 2) * 2 * kHeadDim * 16);
+            const half8 a = read_vt(lds, vb, 0, x >> 2, db);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]), o[db], 0, 0, 0);
         }
         wg_barrier(); // stage 0 is reloaded next
@@ -590,14 +560,11 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         uint32_t koff[2], voff[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            koff[r] = koffset(krow(wave, lane, r), lane);
-            voff[r] = voffset(vkey(tid, r), tid);
+            const int row = krow(wave, lane, r);
+            koff[r] = koffset(row, lane);
+            voff[r] = (uint32_t)(row * ROWB + (((lane & 15) ^ vswz(row)) << 4));
         }
         const uint32_t lds_base = lds_offset(lds);
-        uint32_t vst[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            vst[e] = vstore_offset(tid, e);
 
         // Tile loads.  Rows at or past kend clamp to the last key (finite values; they are
         // masked or carry probability 0), and only the last tile can hold such rows.
@@ -617,18 +584,20 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 dma_k(tile, o, stage_lds, wave);
             }
         };
-        auto issue_v = [&](VRegs &r, int j) {
+        // V rows the same way into the V region of a stage, under their own chunk swizzle
+        auto issue_v = [&](int j, uint32_t stage_lds) {
             const int kb = j * KT;
-            // (readfirstlane keeps the whole tile offset in the scalar base address)
-            const char *tile = vbase + (int64_t)__builtin_amdgcn_readfirstlane(kb) * ROWB;
+            const char *tile = vbase + (int64_t)kb * ROWB;
             if (kb + KT <= kend) {
-                load_v(r, tile, voff);
+                dma_k(tile, voff, stage_lds, wave);
             } else {
                 uint32_t o[2];
 #pragma unroll
-                for (int x = 0; x < 2; ++x)
-                    o[x] = voffset(min(vkey(tid, x), klast - kb), tid);
-                load_v(r, tile, o);
+                for (int r = 0; r < 2; ++r) {
+                    const int row = krow(wave, lane, r);
+                    o[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ vswz(row)) << 4));
+                }
+                dma_k(tile, o, stage_lds, wave);
             }
         };
 
@@ -646,10 +615,9 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         for (int s = 0; s < 8; ++s)
             qin[s] = ld16(qrow + 16 * s + 8 * hh);
         issue_k(0, lds_base);
+        issue_v(0, lds_base + VREG_B);
         if (ntiles > 1)
             issue_k(1, lds_base + TILE_B);
-        VRegs vr;
-        issue_v(vr, 0);
 
         // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16.
         // When the unit's items span at most two token blocks, the workgroup computes each
@@ -667,10 +635,9 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
         // K operand of head-dim step s: chunk (2s + hh) ^ (c % 16) of key row c.  The step
         // sits in bits 5-7 of the byte offset, so one per-lane base serves all eight steps
-        // through an xor.  V^T operand of dim block db: dim row vpos(32 db + c) =
-        // 32 db + (c ^ (c / 8) ^ 4 (db % 2)), i.e. base ^ (64 (db % 2)) plus 512 db bytes.
+        // through an xor.  V^T operands: vt_base.
         const uint32_t kbase0 = (uint32_t)(c * ROWB + ((hh ^ kswz(c)) << 4));
-        const uint32_t vbase0 = (uint32_t)(VREG_B + hh * kHeadDim * 16 + 16 * (c ^ (c >> 3)));
+        const uint32_t vbase0 = vt_base(lane);
 
         floatx16 o[4];
         // row sums of the f16 probabilities, accumulated on the matrix core (every slot of
@@ -697,11 +664,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // (kb, vb: the per-lane bases, made opaque once per phase so that the compiler
         // keeps two registers instead of hoisting twelve precomputed addresses)
         auto rd = [&](uint32_t kb, uint32_t vb, int kso, int vso, int x) -> half8 {
-            if (x < 16) {
-                const int db = x & 3;
-                return *reinterpret_cast<const half8 *>(lds + ((vb ^ (uint32_t)(64 * (db & 1))) + 512 * db + vso +
-                                                               (x >> 2) * 2 * kHeadDim * 16));
-            }
+            if (x < 16)
+                return read_vt(lds, vb, vso, x >> 2, x & 3);
             const int y = x - 16;
             return *reinterpret_cast<const half8 *>(lds + ((kb ^ (uint32_t)((y >> 1) << 5)) + kso + (y & 1) * 32 * ROWB));
         };
@@ -761,21 +725,20 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
         };
 
-        // Tile staging for M(j) (STG = j % 4): tile j+1's V rows (loaded one phase pair ago)
-        // into its stage -- all of this wave's loads are complete afterwards, including its K
-        // share of tile j+1 -- then tile j+2's loads (V rows into registers, K straight into
-        // its stage).  It runs at the end of the softmax phase before M(j), while the SIMD
-        // partner is in its MFMA phase: the stages it writes were last read two phases ago.
+        // Tile staging for M(j) (STG = j % 4): wait for this wave's share of the previous
+        // staging's loads (K of tile j+1, V of tile j), which the barrier ending the phase
+        // then publishes, and start the next: K of tile j+2 and V of tile j+1, each into its
+        // stage.  It runs at the end of the softmax phase before M(j), while the SIMD
+        // partner is in its MFMA phase.  A V stage is refilled one phase pair after its K
+        // stage: V of tile j-3 is read by the PV part of M(j-2), which the trailing group
+        // runs during the leading group's softmax phase S(j-2).
         auto stage_tiles = [&](auto stg_c, int j) {
             constexpr int STG = decltype(stg_c)::value;
-            if (j + 1 < ntiles) {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                store_v<(STG + 1) % NSTAGE>(vr, lds, vst);
-            }
-            if (j + 2 < ntiles) {
-                issue_v(vr, j + 2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (j + 2 < ntiles)
                 issue_k(j + 2, lds_base + (uint32_t)(((STG + 2) % NSTAGE) * TILE_B));
-            }
+            if (j + 1 < ntiles)
+                issue_v(j + 1, lds_base + (uint32_t)(VREG_B + ((STG + 1) % NSTAGE) * TILE_B));
         };
 
         // M(j), 1 <= j < ntiles: PV of tile j-1 and S^T of tile j.  A wave whose tile j-1 is
@@ -855,7 +818,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
             stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
             prefetch(STG * TILE_B);
-            wg_barrier_reads_in_flight<RD>();
+            wg_barrier_reads_in_flight<2 * RD>(); // two transposing reads per V^T operand
         };
 
 #pragma unroll
@@ -863,11 +826,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             o[db] = floatx16{0.f};
         lsum = floatx16{0.f};
 
-        // tile 0 (K and V) into stage 0; tile 1's V rows stay in registers until M(0)
+        // tile 0 (K and V) in stage 0, K of tile 1 in stage 1
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        store_v<0>(vr, lds, vst);
-        if (ntiles > 1)
-            issue_v(vr, 1);
         wg_barrier();
 
         if (grp == 1)
