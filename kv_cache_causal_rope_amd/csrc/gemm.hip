@@ -95,9 +95,24 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmParams p, RopeTable tab)
     const int lane = tid & 63;
     const int tiles_m = (p.rows_u + TM - 1) / TM;
     const int tiles_n = p.n / TN;
-    int b = blockIdx.x;
-    const int tn = b % tiles_n;
-    b /= tiles_n;
+    int b = blockIdx.x, tn;
+    if (EPI == EPI_QKV) {
+        // the k-head tiles (rotation in the epilogue, about twice as long) go first, so
+        // that they are not left for the last round
+        const int nk = p.units * tiles_m * p.hkv;
+        if (b < nk) {
+            tn = p.hq + b % p.hkv;
+            b /= p.hkv;
+        } else {
+            b -= nk;
+            const int others = tiles_n - p.hkv, t = b % others;
+            tn = t < p.hq ? t : t + p.hkv;
+            b /= others;
+        }
+    } else {
+        tn = b % tiles_n;
+        b /= tiles_n;
+    }
     const int tm = b % tiles_m;
     const int u = b / tiles_m;
     const int m0 = tm * TM, n0 = tn * TN;
