@@ -23,8 +23,8 @@
  *             unfused path expands KV heads with repeat_interleave, so query head h
  *             reads KV head floor(h / G).
  *
- * Readings where the pages leave a step open are listed in the design doc; each one is also
- * stated next to the code that takes it.
+ * Where the pages leave a step open, the reading taken is stated next to the code that
+ * takes it.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC (see build.py).
  * Every floating-point step is fp64; f16 appears only at tensor boundaries.
