@@ -640,15 +640,20 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const uint32_t vbase0 = vt_base(lane);
 
         floatx16 o[4];
-        // row sums of the f16 probabilities, accumulated on the matrix core (every slot of
-        // the lane holds the sum for its query)
-        floatx16 lsum;
+        // row sums of the f16 probabilities, accumulated on the matrix core by one
+        // v_mfma_f32_16x16x32_f16 per 16-key step (half the cycles of a 32x32x16): B is the
+        // step's P^T operand read as 16x16x32 B (lane l: column l % 16, k 8 (l / 16) ..),
+        // so column n gathers query n (lane groups 0, 2) and query n + 16 (groups 1, 3);
+        // the A operand (row m, k-group l / 16) is 1 where m % 2 == group % 2, so even rows
+        // of the result sum query n and odd rows query n + 16.  Lane l finds its query's sum
+        // in slot (l / 16) % 2.
+        floatx4 lsum;
         float m_run = 0.f; // reference max (log2 units)
         bool first = true;
         floatx16 sacc[2];  // S^T of the current tile, as (score - m_run)
         u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
-        const half8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
-                            (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+        const _Float16 sel1 = (lane & 1) == ((lane >> 4) & 1) ? (_Float16)1.f : (_Float16)0.f;
+        const half8 sel = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
 
         // Ping-pong: a wave's phases alternate
         //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
@@ -701,9 +706,9 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 if (x < 16) {
                     o[x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(half8, pw[x >> 2]),
                                                                       o[x & 3], 0, 0, 0);
-                    // after the last dim block of key group x/4: its column sums
+                    // after the last dim block of key group x/4: its row sums
                     if ((x & 3) == 3)
-                        lsum = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, __builtin_bit_cast(half8, pw[x >> 2]),
+                        lsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, __builtin_bit_cast(half8, pw[x >> 2]),
                                                                       lsum, 0, 0, 0);
                     if (X1 > 16) {
                         sacc[x >> 3][2 * (x & 7)] = mr;
@@ -824,7 +829,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
         for (int db = 0; db < 4; ++db)
             o[db] = floatx16{0.f};
-        lsum = floatx16{0.f};
+        lsum = floatx4{0.f};
 
         // tile 0 (K and V) in stage 0, K of tile 1 in stage 1
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -867,7 +872,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // An f16 probability past its range made a row sum infinite (or a NaN input made
         // it NaN): the workgroup recomputes the unit on the exact path.  The flag holds the
         // unit, so it never needs clearing.
-        if (__builtin_amdgcn_ballot_w64(row_valid && !(lsum[0] <= 3.0e38f)) != 0 && lane == 0)
+        const float lrow = ((lane >> 4) & 1) ? lsum[1] : lsum[0];
+        if (__builtin_amdgcn_ballot_w64(row_valid && !(lrow <= 3.0e38f)) != 0 && lane == 0)
             ovf_unit = v;
         wg_barrier();
         if (ovf_unit == v) {
@@ -881,7 +887,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // last barrier until the next unit's first K tile 2 load, two barriers later), so
         // that every global store writes whole 256-byte rows instead of 8-byte pieces of 64
         // rows.  16-byte chunk k of row c sits at chunk k ^ (c % 16).
-        const float inv = 1.f / lsum[0];
+        const float inv = 1.f / lrow;
         char *ostage = lds + (wave < 4 ? 2 * TILE_B + wave * (QB * ROWB)
                                        : VREG_B + 2 * TILE_B + (wave - 4) * (QB * ROWB));
         // chunk k of row c: the per-lane base with bits 4-7 flipped by k (opaque, so the
