@@ -41,8 +41,8 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 267.219e6,
-        "src": ("4ba0093e342897695dc8b25d0999e197beb4d4b559f9eb4aa9dc0799ed03e428",
+        "bytes": 267.407e6,
+        "src": ("12abee6e1d6421ceaeab530940b87c00a6bbe19002417370de3ce5de3b625815",
                 "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
                 "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
     "decode_split:qwen1p5b_decode_l4096_b32": {
