@@ -1,6 +1,7 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                    [--no-projections] [--no-extra-workloads]
 
 One step is one attn_prefill call (rotary embedding of k + cache append, then causal GQA
 flash attention with q rotated in the kernel prologue) over the 28-layer, T = 1024,
@@ -13,6 +14,11 @@ attn_decode step on the 28-layer batch-32 (4096-row) workload and on the 4-layer
 batch-64 YaRN long-context workload -- with the 256 MB Infinity Cache flushed (a full
 read of a 512 MB buffer) before every timed step; decode bytes count the cache rows read plus the new k/v read, the
 appended row written and q read / out written.
+
+Unless --no-extra-workloads is given, it also reports the prefill_kv workload (32 layers,
+256 new tokens after 3840 cached rows, 32q/2kv; `prefill_kv`, TFLOP/s as above) and the
+single-sequence decode workloads (28 layers, caches to 1024 and to 4096 rows; extra
+`decode` entries, launch-dominated).
 
 `roofline` describes the dominant kernel (the prefill flash kernel), timed per launch
 with HIP events the library records around it on the launch stream; `cpu_baseline` is
@@ -287,6 +293,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-projections", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the prefill_kv workload (32 layers, 256 new tokens after 3840 cached "
+                         "rows) and the single-sequence decode workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -321,9 +330,28 @@ def main():
         f"{value:.1f} TFLOP/s step, {achieved:.1f} TFLOP/s kernel")
     torch.cuda.empty_cache()
 
+    pkv = None
+    if not args.no_extra_workloads:
+        name = "h4096_prefill_kv_3840p256"
+        log(f"[bench] prefill_kv {name}")
+        pcfg, p_ms, pk_ms, pflops = bench_prefill(kv, W, name, max(5, args.steps // 2), min(args.warmup, 3))
+        pkv = {"workload": name, "value": round(pflops / (p_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+               "ms_per_step": round(p_ms, 5), "flops_per_step": pflops,
+               "roofline": {"bound": "mfma", "achieved": round(pflops / (pk_ms * 1e-3) / 1e12, 2),
+                            "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(pflops / (pk_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                            "traffic": traffic("prefill_attn", name)}}
+        log(f"[bench] prefill_kv: {p_ms * 1e3:.1f} us/step, flash kernel {pk_ms * 1e3:.1f} us, "
+            f"{pkv['value']:.1f} TFLOP/s step, {pkv['roofline']['achieved']:.1f} TFLOP/s kernel")
+        torch.cuda.empty_cache()
+
     decode = []
     if not args.no_decode:
-        for name in ["qwen1p5b_decode_l4096_b32", "yarn_decode_l32k_b64"]:
+        # the two large decode workloads, then the single-sequence ones (launch-dominated)
+        names = ["qwen1p5b_decode_l4096_b32", "yarn_decode_l32k_b64"]
+        if not args.no_extra_workloads:
+            names += ["qwen1p5b_decode_l1024_b1", "qwen1p5b_decode_l4096_b1"]
+        for name in names:
             log(f"[bench] decode {name}")
             dcfg, call_ms, dk_ms, nbytes, ceil_gbs = bench_decode(kv, W, name, max(3, args.steps // 2),
                                                                   min(args.warmup, 3))
@@ -380,6 +408,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                      "traffic": traffic("prefill_attn", cfg.name)},
+        "prefill_kv": pkv,
         "decode": decode,
         "projections": proj,
         "measured_ceilings": ceilings,
