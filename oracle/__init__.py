@@ -91,6 +91,30 @@ def _c_rope(rp: RopeParams) -> _CRope:
     return c
 
 
+def _c_rope_sets(rp, unit_set, n: int):
+    """(C array of parameter blocks, keep-alive list, unit_set int32 array or None).
+
+    rp is one RopeParams (every unit) or a sequence of them with unit_set [n] naming the
+    set each unit uses."""
+    sets = [rp] if isinstance(rp, RopeParams) else list(rp)
+    if not sets:
+        raise ValueError("at least one rotary parameter set is needed")
+    arr = (_CRope * len(sets))()
+    keep = []
+    for i, s in enumerate(sets):
+        c = _c_rope(s)
+        keep.append(c)
+        arr[i] = c
+    if unit_set is None:
+        if len(sets) != 1:
+            raise ValueError("several parameter sets need unit_set")
+        return arr, keep, None
+    us = np.ascontiguousarray(np.asarray(unit_set, dtype=np.int32))
+    if us.shape != (n,) or us.min(initial=0) < 0 or us.max(initial=0) >= len(sets):
+        raise ValueError("unit_set must be [n] indices into the parameter sets")
+    return arr, keep, us
+
+
 _P = ctypes.c_void_p
 
 
@@ -115,13 +139,10 @@ def load(path: str) -> ctypes.CDLL:
     L.ora_append.argtypes = [_P, _P, _P, _P, _P] + [ctypes.c_int] * 5
     L.ora_prefill_kv.restype = ctypes.c_int
     L.ora_prefill_kv.argtypes = ([_P] * 8 + [ctypes.c_int] * 6 +
-                                 [ctypes.c_double, ctypes.POINTER(_CRope), _P, _P])
+                                 [ctypes.c_double, _P, _P, _P, _P])
     L.ora_decode.restype = ctypes.c_int
     L.ora_decode.argtypes = ([_P] * 8 + [ctypes.c_int] * 5 +
-                             [ctypes.c_double, ctypes.POINTER(_CRope), _P, _P])
-    L.ora_decode_rows.argtypes = ([_P] * 6 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                              ctypes.c_int, ctypes.c_int64,
-                                              ctypes.c_double, _P])
+                             [ctypes.c_double, _P, _P, _P, _P])
     L.ora_num_threads.restype = ctypes.c_int
     return L
 
@@ -274,8 +295,9 @@ def append(cache_k: np.ndarray, cache_v: np.ndarray, k, v, lens) -> None:
 
 # ---------------------------------------------------------------- attention
 def prefill_kv(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens,
-               scale: float, rp: RopeParams):
-    """Chunked prefill over a history.  Caches are updated in place.
+               scale: float, rp, unit_set=None):
+    """Chunked prefill over a history.  Caches are updated in place.  rp: one RopeParams,
+    or a list of them with unit_set [n] choosing each unit's set.
 
     Returns (out f16 bits [n,t,hq,d], out fp64, rotated k fp64 [n,t,hkv,d])."""
     q, k, v = _u16(q), _u16(k), _u16(v)
@@ -291,17 +313,18 @@ def prefill_kv(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, len
     out = np.empty(q.shape, dtype=np.uint16)
     out64 = np.empty(q.shape, dtype=np.float64)
     k64 = np.empty(k.shape, dtype=np.float64)
-    c = _c_rope(rp)
+    sets, _keep, us = _c_rope_sets(rp, unit_set, n)
     rc = lib().ora_prefill_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cache_k),
                               _ptr(cache_v), _ptr(lens), _ptr(out), n, t, hq, hkv, d, s_cap,
-                              float(scale), ctypes.byref(c), _ptr(out64), _ptr(k64))
+                              float(scale), ctypes.cast(sets, ctypes.c_void_p),
+                              None if us is None else _ptr(us), _ptr(out64), _ptr(k64))
     if rc != 0:
         raise ValueError("oracle prefill_kv: shape or capacity error")
     return out, out64, k64
 
 
 def prefill_kv_varlen(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens, new_lens,
-                      scale: float, rp: RopeParams):
+                      scale: float, rp, unit_set=None):
     """prefill_kv over a batch whose unit u brings new_lens[u] new tokens (rows past it are
     padding): unit u is prefill_kv of that unit alone on its first new_lens[u] rows ([Sophgo]
     Listing 2 per sequence).  Caches are updated in place.  Returns (out bits, out fp64,
@@ -319,21 +342,24 @@ def prefill_kv_varlen(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarr
         if tu == 0:
             continue
         ck, cv = np.ascontiguousarray(cache_k[u:u + 1]), np.ascontiguousarray(cache_v[u:u + 1])
+        rpu = rp if unit_set is None else list(rp)[int(unit_set[u])]
         o, o64, kk = prefill_kv(q[u:u + 1, :tu], k[u:u + 1, :tu], v[u:u + 1, :tu], pos[u:u + 1, :tu],
-                                ck, cv, lens[u:u + 1], scale, rp)
+                                ck, cv, lens[u:u + 1], scale, rpu)
         cache_k[u], cache_v[u] = ck[0], cv[0]
         out[u, :tu], out64[u, :tu], k64[u, :tu] = o[0], o64[0], kk[0]
     return out, out64, k64
 
 
-def prefill(q, k, v, positions, cache_k, cache_v, scale: float, rp: RopeParams):
+def prefill(q, k, v, positions, cache_k, cache_v, scale: float, rp, unit_set=None):
     n = np.asarray(q).shape[0]
-    return prefill_kv(q, k, v, positions, cache_k, cache_v, np.zeros(n, np.int32), scale, rp)
+    return prefill_kv(q, k, v, positions, cache_k, cache_v, np.zeros(n, np.int32), scale, rp,
+                      unit_set)
 
 
 def decode(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens, scale: float,
-           rp: RopeParams):
-    """One decode step.  q: [n, hq, d]; k, v: [n, hkv, d]; positions, lens: [n].
+           rp, unit_set=None):
+    """One decode step.  q: [n, hq, d]; k, v: [n, hkv, d]; positions, lens: [n].  rp and
+    unit_set as for prefill_kv.
 
     Caches are updated in place (row lens[n]).  Returns (out bits [n,hq,d], out fp64,
     rotated k fp64 [n,hkv,d])."""
@@ -348,27 +374,12 @@ def decode(q, k, v, positions, cache_k: np.ndarray, cache_v: np.ndarray, lens, s
     out = np.empty(q.shape, dtype=np.uint16)
     out64 = np.empty(q.shape, dtype=np.float64)
     k64 = np.empty(k.shape, dtype=np.float64)
-    c = _c_rope(rp)
+    sets, _keep, us = _c_rope_sets(rp, unit_set, n)
     rc = lib().ora_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(cache_k), _ptr(cache_v),
                           _ptr(lens), _ptr(out), n, hq, hkv, d, s_cap, float(scale),
-                          ctypes.byref(c), _ptr(out64), _ptr(k64))
+                          ctypes.cast(sets, ctypes.c_void_p), None if us is None else _ptr(us),
+                          _ptr(out64), _ptr(k64))
     if rc != 0:
         raise ValueError("oracle decode: shape or capacity error")
     return out, out64, k64
 
-
-def decode_rows(q_rot, cache_k: np.ndarray, cache_v: np.ndarray, units, heads, lens_s,
-                hq: int, scale: float) -> np.ndarray:
-    """Sampled decode attention: for sample i, unit units[i], query head heads[i] with
-    rotated query q_rot[i] attends over rows 0..lens_s[i] of its KV head in caches that
-    already hold the appended row.  Returns fp64 [ns, d]."""
-    q_rot = _u16(q_rot)
-    us, hs, ls = _i32(units), _i32(heads), _i32(lens_s)
-    ns, d = q_rot.shape
-    n, hkv, s_cap, d2 = cache_k.shape
-    assert d2 == d and us.shape == (ns,) and hs.shape == (ns,) and ls.shape == (ns,)
-    assert np.all(ls + 1 <= s_cap) and np.all(us < n) and np.all(hs < hq)
-    out = np.empty((ns, d), dtype=np.float64)
-    lib().ora_decode_rows(_ptr(q_rot), _ptr(cache_k), _ptr(cache_v), _ptr(us), _ptr(hs),
-                          _ptr(ls), ns, hq, hkv, d, s_cap, float(scale), _ptr(out))
-    return out

@@ -13,7 +13,8 @@
  *             mask), sec. 3.1 Listings 1-2 (block without / with history_k, history_v),
  *             sec. 4.1 (the prefill / prefill_kv / decode split).
  *   [ds4]     "ds4.c study notes", Part 4, section 1, Trace 1 (YaRN ramp and correction
- *             dims) and Trace 2 (tail RoPE rotation, rotation matrix, theta schedule).
+ *             dims) and Trace 2 (tail RoPE rotation, rotation matrix, theta schedule,
+ *             per-layer frequency base / scale with the ramp only on compressed layers).
  *   [Buddy]   "Buddy-MLIR DeepSeek model import, compilation and inference scheduling"
  *             (juejin), sec. 6.4.3 (KV cache [B, kv_heads, max_len, head_dim], f16),
  *             sec. 6.4.5-6.4.6 (cache hand-off: position = prompt length, +1 per step),
@@ -27,8 +28,11 @@
  * takes it.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC (see build.py).
- * Every floating-point step is fp64; f16 appears only at tensor boundaries.
+ * Every floating-point step is fp64; f16 appears only at tensor boundaries.  The
+ * attention loops decode each (unit, KV head) slab of the cache to fp64 once and then
+ * sum every dot product and every weighted sum in ascending index order.
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -104,6 +108,54 @@ void ora_f64_to_f16_array(const double *x, uint16_t *out, int64_t n)
         out[i] = ora_f64_to_f16(x[i]);
 }
 
+/* The value of every f16 bit pattern, filled once by ora_f16_to_f64 itself: a lookup in
+ * it is that function's result, not a second decoder. */
+static double g_f16_value[65536];
+static int g_f16_value_ready;
+
+static void ora_fill_f16_values(void)
+{
+    if (g_f16_value_ready)
+        return;
+    for (int b = 0; b < 65536; ++b)
+        g_f16_value[b] = ora_f16_to_f64((uint16_t)b);
+    g_f16_value_ready = 1;
+}
+
+/* rows [0, rows) of a [*, d] f16 slab to fp64 */
+static void ora_slab_to_f64(const uint16_t *src, int64_t rows, int d, double *dst)
+{
+    for (int64_t i = 0; i < rows * (int64_t)d; ++i)
+        dst[i] = g_f16_value[src[i]];
+}
+
+/* the same, transposed: dst[i * rows + j] = row j, dim i (64 rows at a time, so that
+ * both sides of the copy stay in cache) */
+static void ora_slab_to_f64_t(const uint16_t *src, int64_t rows, int d, double *dst)
+{
+    for (int64_t j0 = 0; j0 < rows; j0 += 64) {
+        const int64_t j1 = j0 + 64 < rows ? j0 + 64 : rows;
+        for (int i = 0; i < d; ++i)
+            for (int64_t j = j0; j < j1; ++j)
+                dst[(int64_t)i * rows + j] = g_f16_value[src[j * d + i]];
+    }
+}
+
+/* dot[j] = <q, key j> for keys j < nk of a transposed slab kt [d][stride]: the scores of
+ * all keys are accumulated one head dim at a time, so each dot product sums its d terms
+ * in ascending dim order. */
+static void ora_scores(const double *q, const double *kt, int64_t stride, int64_t nk, int d, double *dot)
+{
+    for (int64_t j = 0; j < nk; ++j)
+        dot[j] = 0.0;
+    for (int i = 0; i < d; ++i) {
+        const double qi = q[i];
+        const double *ki = kt + (int64_t)i * stride;
+        for (int64_t j = 0; j < nk; ++j)
+            dot[j] += qi * ki[j];
+    }
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Rotary embedding parameters and per-pair frequencies.                                 */
 /* ------------------------------------------------------------------------------------ */
@@ -127,25 +179,29 @@ typedef struct ora_rope_params {
 } ora_rope_params;
 
 /* [ds4] Trace 1: the dimension index at which a pair turns `beta` full circles over the
- * original context: n_dims * ln(n_ctx_orig / (2 pi beta)) / (2 ln base).
- * Reading: n_dims is the rotated width n_rot; the value is used unrounded and unclamped
- * (the page elides the body of the two-boundary helper). */
+ * original context.  A pair of frequency base^(-2 x / n_dims) turns
+ * n_ctx_orig * base^(-2 x / n_dims) / (2 pi) times over n_ctx_orig positions; setting
+ * that count to beta and solving for x gives
+ *     x = n_dims * ln(n_ctx_orig / (2 pi beta)) / (2 ln base).
+ * Reading: n_dims is the rotated width n_rot; x is used unrounded and unclamped (the page
+ * elides the body of the two-boundary helper). */
 double ora_yarn_corr_dim(int n_dims, int n_ctx_orig, double beta, double base)
 {
     return (double)n_dims * log((double)n_ctx_orig / (2.0 * M_PI * beta)) / (2.0 * log(base));
 }
 
-/* [ds4] Trace 1: ramp over the pair index j = i0/2: 1 below `low` (keep the original
- * frequency), 0 above `high` (fully scaled), linear in between.  The denominator is
- * floored at 0.001 as on the page. */
+/* [ds4] Trace 1: the ramp over the pair index j (= i0/2) is 1 up to `low` (the pair keeps
+ * its original frequency), 0 from low + width on (fully interpolated) and falls linearly
+ * in between; width = high - low, floored at 0.001 as on the page. */
 double ora_yarn_ramp(double low, double high, int j)
 {
-    double y = ((double)j - low) / fmax(0.001, high - low);
-    if (y < 0.0)
-        y = 0.0;
-    if (y > 1.0)
-        y = 1.0;
-    return 1.0 - y;
+    const double width = fmax(0.001, high - low);
+    const double along = ((double)j - low) / width; /* 0 at low, 1 at low + width */
+    if (along <= 0.0)
+        return 1.0;
+    if (along >= 1.0)
+        return 0.0;
+    return 1.0 - along;
 }
 
 /* Per-pair effective angular frequency omega_eff[j], j = 0 .. n_rot/2 - 1.
@@ -183,70 +239,81 @@ void ora_rope_freqs(const ora_rope_params *rp, double *omega_eff, double *gamma_
     }
 }
 
-/* Rotate rows of x in place of a copy.
+/* Rotate rows of x into out.
  * x, out: f16 [rows, h, d] (row-major, d innermost); positions: [rows].
- * [ds4] Trace 2 rotation of pair j of a head, (x0, x1), o = d - n_rot:
- *     c = cos(theta) * mscale,  s = sin_sign * sin(theta) * mscale,
- *     x0' = x0 * c - x1 * s,    x1' = x0 * s + x1 * c
- * i.e. the matrix [[cos, -sin], [sin, cos]] applied to the pair.
+ * [ds4] Trace 2 turns each rotated pair by theta and scales it by mscale: read as a
+ * complex number z = x0 + i x1, the pair becomes z * mscale * e^(i theta) (the rotation
+ * matrix [[cos, -sin], [sin, cos]] of the page is multiplication by e^(i theta)).
  * Reading: the rotated dims are the last n_rot dims of each head (the page's pointer to
  * the head start contradicts its own "tail" wording and the tail-rotation workload).
  * Pairs: (x[o + 2j], x[o + 2j + 1]) as printed on the page (pairing 0), or
  * (x[o + j], x[o + j + n_rot/2]) (pairing 1, the half-split convention of many
- * checkpoints; the same rotation on a permuted pairing).
- * sin_sign: [ds4] Trace 2 passes an `inverse` flag and multiplies sin by sin_sign; the
- * excerpt omits its definition.  Reading: sin_sign = -1 when inverse, else +1.
+ * checkpoints; the same rotation on a permuted pairing), o = d - n_rot.
+ * Direction: [ds4] Trace 2 passes an `inverse` flag and a sign on the sine it does not
+ * define.  Reading: the inverse rotation turns by -theta (z * mscale * e^(-i theta)).
  * Tables: [Sophgo] Listings 1-2 gather precomputed cos / sin by position_ids
  * (top.Gather(rotary_cos_w, pos_ids)) and hand them to top.Rope.  Reading: one value per
- * rotated pair, rows indexed by position; the gathered values are the whole factor (no
- * mscale); sin_sign still applies.  A position outside [0, table_rows) makes that row's
- * rotated dims NaN.
+ * rotated pair, rows indexed by position; the gathered (cos, sin) is the whole factor
+ * (cos + i sin, no mscale), conjugated for the inverse rotation.  A position outside
+ * [0, table_rows) makes that row's rotated dims NaN.
  * Dims [0, o) are copied bit for bit.  out64 (optional) gets the unrounded fp64 values. */
 void ora_rope(const uint16_t *x, const int32_t *positions, int64_t rows, int h, int d,
               const ora_rope_params *rp, uint16_t *out, double *out64)
 {
     const int half = rp->n_rot / 2;
     const int o = d - rp->n_rot;
-    const double sin_sign = rp->inverse ? -1.0 : 1.0;
     double *omega = (double *)malloc(sizeof(double) * (size_t)(half > 0 ? half : 1));
     ora_rope_freqs(rp, omega, NULL, NULL);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-        const double pos = (double)positions[r];
-        const int in_table = rp->cos_table && positions[r] >= 0 && positions[r] < rp->table_rows;
+        const int p = positions[r];
+        double complex factor[half > 0 ? half : 1];
+        /* the factor of each rotated pair at this position (a quiet NaN for a position
+           the table does not hold) */
+        const int in_table = !rp->cos_table || (p >= 0 && p < rp->table_rows);
+        for (int j = 0; j < half && !in_table; ++j)
+            factor[j] = CMPLX(NAN, NAN);
+        for (int j = 0; j < half && in_table; ++j) {
+            double complex f;
+            if (rp->cos_table) {
+                f = CMPLX((double)rp->cos_table[(int64_t)p * half + j],
+                          (double)rp->sin_table[(int64_t)p * half + j]);
+            } else {
+                const double theta = (double)p * omega[j];
+                f = rp->mscale * CMPLX(cos(theta), sin(theta));
+            }
+            factor[j] = rp->inverse ? conj(f) : f;
+        }
         for (int hh = 0; hh < h; ++hh) {
-            const int64_t base_idx = (r * h + hh) * (int64_t)d;
+            const int64_t head = (r * h + hh) * (int64_t)d;
             for (int i = 0; i < o; ++i) {
-                out[base_idx + i] = x[base_idx + i];
+                out[head + i] = x[head + i];
                 if (out64)
-                    out64[base_idx + i] = ora_f16_to_f64(x[base_idx + i]);
+                    out64[head + i] = ora_f16_to_f64(x[head + i]);
             }
             for (int j = 0; j < half; ++j) {
-                double c, s;
-                if (rp->cos_table) {
-                    c = in_table ? (double)rp->cos_table[(int64_t)positions[r] * half + j] : NAN;
-                    s = in_table ? sin_sign * (double)rp->sin_table[(int64_t)positions[r] * half + j] : NAN;
-                } else {
-                    const double theta = pos * omega[j];
-                    c = cos(theta) * rp->mscale;
-                    s = sin_sign * sin(theta) * rp->mscale;
-                }
-                const int64_t i0 = base_idx + o + (rp->pairing ? j : 2 * j);
-                const int64_t i1 = i0 + (rp->pairing ? half : 1);
-                const double x0 = ora_f16_to_f64(x[i0]);
-                const double x1 = ora_f16_to_f64(x[i1]);
-                const double y0 = x0 * c - x1 * s;
-                const double y1 = x0 * s + x1 * c;
-                out[i0] = ora_f64_to_f16(y0);
-                out[i1] = ora_f64_to_f16(y1);
+                const int64_t re_at = head + o + (rp->pairing ? j : 2 * j);
+                const int64_t im_at = rp->pairing ? re_at + half : re_at + 1;
+                const double complex z = CMPLX(ora_f16_to_f64(x[re_at]), ora_f16_to_f64(x[im_at]));
+                const double complex w = z * factor[j];
+                out[re_at] = ora_f64_to_f16(creal(w));
+                out[im_at] = ora_f64_to_f16(cimag(w));
                 if (out64) {
-                    out64[i0] = y0;
-                    out64[i1] = y1;
+                    out64[re_at] = creal(w);
+                    out64[im_at] = cimag(w);
                 }
             }
         }
     }
     free(omega);
+}
+
+/* The parameter set unit u rotates with: sets[unit_set[u]] ([ds4] Part 4 sec. 1, Trace 2:
+ * each layer carries its own frequency base and scale, and only the compressed layers
+ * turn the YaRN ramp on), or sets[0] for every unit when unit_set is NULL. */
+static const ora_rope_params *ora_unit_params(const ora_rope_params *sets, const int32_t *unit_set, int u)
+{
+    return unit_set ? &sets[unit_set[u]] : &sets[0];
 }
 
 /* [Buddy] sec. 6.4.5 / [Sophgo] Listing 2 (Concat(history, new)):
@@ -270,13 +337,27 @@ int ora_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k, const ui
     return 0;
 }
 
+/* rotate q [n, t, hq, d] and k [n, t, hkv, d] unit by unit, each unit with its own set */
+static void ora_rope_units(const uint16_t *q, const uint16_t *k, const int32_t *positions, int n, int t,
+                           int hq, int hkv, int d, const ora_rope_params *sets, const int32_t *unit_set,
+                           uint16_t *qh, uint16_t *kh, double *k64)
+{
+    for (int u = 0; u < n; ++u) {
+        const ora_rope_params *rp = ora_unit_params(sets, unit_set, u);
+        const int64_t qo = (int64_t)u * t * hq * d, ko = (int64_t)u * t * hkv * d;
+        ora_rope(q + qo, positions + (int64_t)u * t, t, hq, d, rp, qh + qo, NULL);
+        ora_rope(k + ko, positions + (int64_t)u * t, t, hkv, d, rp, kh + ko, k64 ? k64 + ko : NULL);
+    }
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Attention.                                                                            */
 /* ------------------------------------------------------------------------------------ */
 
 /* prefill_kv ([Sophgo] Listing 2 and sec. 4.1; prefill is the case lens == 0, Listing 1):
- *   1. rotate q and k at their positions; the rotated q and k are rounded to f16 because
- *      the Rope op hands f16 tensors to the attention op in an f16 model;
+ *   1. rotate q and k at their positions, each unit with its parameter set; the rotated
+ *      q and k are rounded to f16 because the Rope op hands f16 tensors to the attention
+ *      op in an f16 model;
  *   2. append rotated k and raw v at rows [lens[n], lens[n] + t) of the cache;
  *   3. for query token tt of unit n and query head hq, with g = hq / (h_q / h_kv)
  *      ([CGDR] repeat_interleave head mapping), attend over cache rows j = 0 .. lens[n]+tt
@@ -285,54 +366,51 @@ int ora_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k, const ui
  * This implementation builds the full masked score matrix of each (unit, head) and then
  * normalises each row; the decode function below is written as a per-query loop instead.
  * q, out: [n, t, hq, d]; k, v: [n, t, hkv, d]; positions: [n, t]; lens: [n] (host);
- * caches: [n, hkv, s_cap, d] (updated in place).  out64 (optional): unrounded output.
- * k64 (optional): unrounded rotated k, [n, t, hkv, d].  Returns 0, or -1 on a capacity
- * or shape error (nothing written). */
+ * caches: [n, hkv, s_cap, d] (updated in place); sets / unit_set: see ora_unit_params.
+ * out64 (optional): unrounded output.  k64 (optional): unrounded rotated k,
+ * [n, t, hkv, d].  Returns 0, or -1 on a capacity or shape error (nothing written). */
 int ora_prefill_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                    const int32_t *positions, uint16_t *cache_k, uint16_t *cache_v,
                    const int32_t *lens, uint16_t *out, int n, int t, int hq, int hkv, int d,
-                   int s_cap, double scale, const ora_rope_params *rp, double *out64,
-                   double *k64)
+                   int s_cap, double scale, const ora_rope_params *sets, const int32_t *unit_set,
+                   double *out64, double *k64)
 {
     if (hkv <= 0 || hq % hkv != 0)
         return -1;
     for (int u = 0; u < n; ++u)
         if (lens[u] < 0 || (int64_t)lens[u] + t > s_cap)
             return -1;
+    ora_fill_f16_values();
     const int G = hq / hkv;
     const int64_t qn = (int64_t)n * t * hq * d, kn = (int64_t)n * t * hkv * d;
     uint16_t *qh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(qn > 0 ? qn : 1));
     uint16_t *kh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(kn > 0 ? kn : 1));
-    ora_rope(q, positions, (int64_t)n * t, hq, d, rp, qh, NULL);
-    ora_rope(k, positions, (int64_t)n * t, hkv, d, rp, kh, k64);
+    ora_rope_units(q, k, positions, n, t, hq, hkv, d, sets, unit_set, qh, kh, k64);
     ora_append(cache_k, cache_v, kh, v, lens, n, t, hkv, d, s_cap);
 
-#pragma omp parallel for collapse(2) schedule(static)
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int u = 0; u < n; ++u) {
         for (int h = 0; h < hq; ++h) {
             const int g = h / G;
             const int L = lens[u] + t; /* keys visible to the last query */
-            const uint16_t *Kc = cache_k + ((int64_t)u * hkv + g) * s_cap * d;
-            const uint16_t *Vc = cache_v + ((int64_t)u * hkv + g) * s_cap * d;
-            double *S = (double *)malloc(sizeof(double) * (size_t)t * (size_t)(L > 0 ? L : 1));
+            const int64_t Lr = L > 0 ? L : 1;
+            double *Kd = (double *)malloc(sizeof(double) * (size_t)(Lr * d));
+            double *Vd = (double *)malloc(sizeof(double) * (size_t)(Lr * d));
+            double *S = (double *)malloc(sizeof(double) * (size_t)t * (size_t)Lr);
             double *qd = (double *)malloc(sizeof(double) * (size_t)d);
-            /* masked score matrix */
+            double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+            ora_slab_to_f64_t(cache_k + ((int64_t)u * hkv + g) * s_cap * d, L, d, Kd);
+            ora_slab_to_f64(cache_v + ((int64_t)u * hkv + g) * s_cap * d, L, d, Vd);
+            /* masked score matrix: keys j <= lens + tt are visible to query tt */
             for (int tt = 0; tt < t; ++tt) {
-                const uint16_t *qrow = qh + (((int64_t)u * t + tt) * hq + h) * d;
-                for (int i = 0; i < d; ++i)
-                    qd[i] = ora_f16_to_f64(qrow[i]);
-                for (int j = 0; j < L; ++j) {
-                    if (j > lens[u] + tt) {
-                        S[(int64_t)tt * L + j] = -INFINITY;
-                        continue;
-                    }
-                    double acc = 0.0;
-                    for (int i = 0; i < d; ++i)
-                        acc += qd[i] * ora_f16_to_f64(Kc[(int64_t)j * d + i]);
-                    S[(int64_t)tt * L + j] = scale * acc;
-                }
+                double *row = S + (int64_t)tt * L;
+                const int nvis = lens[u] + tt + 1;
+                ora_slab_to_f64(qh + (((int64_t)u * t + tt) * hq + h) * d, 1, d, qd);
+                ora_scores(qd, Kd, L, nvis, d, row);
+                for (int j = 0; j < L; ++j)
+                    row[j] = (j < nvis) ? scale * row[j] : -INFINITY;
             }
-            /* row softmax and P V */
+            /* row softmax, then P V (each output dim summed over keys in ascending order) */
             for (int tt = 0; tt < t; ++tt) {
                 double *row = S + (int64_t)tt * L;
                 double mx = -INFINITY;
@@ -346,18 +424,25 @@ int ora_prefill_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 }
                 for (int j = 0; j < L; ++j)
                     row[j] /= sum;
+                for (int i = 0; i < d; ++i)
+                    acc[i] = 0.0;
+                for (int j = 0; j < L; ++j) {
+                    const double *vr = Vd + (int64_t)j * d;
+                    for (int i = 0; i < d; ++i)
+                        acc[i] += row[j] * vr[i];
+                }
                 uint16_t *orow = out + (((int64_t)u * t + tt) * hq + h) * d;
                 for (int i = 0; i < d; ++i) {
-                    double acc = 0.0;
-                    for (int j = 0; j < L; ++j)
-                        acc += row[j] * ora_f16_to_f64(Vc[(int64_t)j * d + i]);
-                    orow[i] = ora_f64_to_f16(acc);
+                    orow[i] = ora_f64_to_f16(acc[i]);
                     if (out64)
-                        out64[(((int64_t)u * t + tt) * hq + h) * d + i] = acc;
+                        out64[(((int64_t)u * t + tt) * hq + h) * d + i] = acc[i];
                 }
             }
+            free(acc);
             free(qd);
             free(S);
+            free(Vd);
+            free(Kd);
         }
     }
     free(qh);
@@ -367,26 +452,28 @@ int ora_prefill_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 
 /* decode ([Sophgo] sec. 4.1: one query per sequence, attending over every earlier key;
  * [Buddy] sec. 6.4.5-6.4.6: the new token sits at the current cache length, which then
- * grows by one).  For unit n: rotate q[n] and k[n] at positions[n], write the rotated k
- * and v at cache row lens[n], then for each query head attend over rows 0 .. lens[n].
- * Written as a per-query loop over the cache (max, then exp-sum, then weighted sum).
+ * grows by one).  For unit n: rotate q[n] and k[n] at positions[n] (with the unit's
+ * parameter set), write the rotated k and v at cache row lens[n], then for each query
+ * head attend over rows 0 .. lens[n].  Written as a per-query loop over the cache (max,
+ * then exp-sum, then weighted sum).
  * q, out: [n, hq, d]; k, v: [n, hkv, d]; positions, lens: [n] (host).
  * Returns 0, or -1 (nothing written) on a capacity / shape error. */
 int ora_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                const int32_t *positions, uint16_t *cache_k, uint16_t *cache_v,
                const int32_t *lens, uint16_t *out, int n, int hq, int hkv, int d, int s_cap,
-               double scale, const ora_rope_params *rp, double *out64, double *k64)
+               double scale, const ora_rope_params *sets, const int32_t *unit_set, double *out64,
+               double *k64)
 {
     if (hkv <= 0 || hq % hkv != 0)
         return -1;
     for (int u = 0; u < n; ++u)
         if (lens[u] < 0 || (int64_t)lens[u] + 1 > s_cap)
             return -1;
+    ora_fill_f16_values();
     const int G = hq / hkv;
     uint16_t *qh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)((int64_t)n * hq * d + 1));
     uint16_t *kh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)((int64_t)n * hkv * d + 1));
-    ora_rope(q, positions, n, hq, d, rp, qh, NULL);
-    ora_rope(k, positions, n, hkv, d, rp, kh, k64);
+    ora_rope_units(q, k, positions, n, 1, hq, hkv, d, sets, unit_set, qh, kh, k64);
     ora_append(cache_k, cache_v, kh, v, lens, n, 1, hkv, d, s_cap);
 
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
@@ -394,29 +481,28 @@ int ora_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         for (int h = 0; h < hq; ++h) {
             const int g = h / G;
             const int nk = lens[u] + 1;
-            const uint16_t *Kc = cache_k + ((int64_t)u * hkv + g) * s_cap * d;
-            const uint16_t *Vc = cache_v + ((int64_t)u * hkv + g) * s_cap * d;
-            const uint16_t *qrow = qh + ((int64_t)u * hq + h) * d;
+            double *Kd = (double *)malloc(sizeof(double) * (size_t)nk * (size_t)d);
+            double *Vd = (double *)malloc(sizeof(double) * (size_t)nk * (size_t)d);
             double *qd = (double *)malloc(sizeof(double) * (size_t)d);
             double *s = (double *)malloc(sizeof(double) * (size_t)nk);
             double *acc = (double *)calloc((size_t)d, sizeof(double));
-            for (int i = 0; i < d; ++i)
-                qd[i] = ora_f16_to_f64(qrow[i]);
+            ora_slab_to_f64_t(cache_k + ((int64_t)u * hkv + g) * s_cap * d, nk, d, Kd);
+            ora_slab_to_f64(cache_v + ((int64_t)u * hkv + g) * s_cap * d, nk, d, Vd);
+            ora_slab_to_f64(qh + ((int64_t)u * hq + h) * d, 1, d, qd);
+            ora_scores(qd, Kd, nk, nk, d, s);
             double mx = -INFINITY;
             for (int j = 0; j < nk; ++j) {
-                double dot = 0.0;
-                for (int i = 0; i < d; ++i)
-                    dot += qd[i] * ora_f16_to_f64(Kc[(int64_t)j * d + i]);
-                s[j] = scale * dot;
+                s[j] = scale * s[j];
                 if (s[j] > mx)
                     mx = s[j];
             }
             double denom = 0.0;
             for (int j = 0; j < nk; ++j) {
                 const double e = exp(s[j] - mx);
+                const double *vr = Vd + (int64_t)j * d;
                 denom += e;
                 for (int i = 0; i < d; ++i)
-                    acc[i] += e * ora_f16_to_f64(Vc[(int64_t)j * d + i]);
+                    acc[i] += e * vr[i];
             }
             uint16_t *orow = out + ((int64_t)u * hq + h) * d;
             for (int i = 0; i < d; ++i) {
@@ -428,52 +514,13 @@ int ora_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
             free(acc);
             free(s);
             free(qd);
+            free(Vd);
+            free(Kd);
         }
     }
     free(qh);
     free(kh);
     return 0;
-}
-
-/* Decode attention for a subset of (unit, head) rows only, reading a cache that already
- * holds the appended row (used to check very large workloads by sampling).  For each
- * sample i: unit us[i], head hs[i]; q_rot: that row's rotated f16 query [d].
- * Attends over cache rows 0 .. lens_s[i] (inclusive) of KV head hs[i] / G. */
-void ora_decode_rows(const uint16_t *q_rot, const uint16_t *cache_k, const uint16_t *cache_v,
-                     const int32_t *us, const int32_t *hs, const int32_t *lens_s, int64_t ns,
-                     int hq, int hkv, int d, int64_t s_cap, double scale, double *out64)
-{
-    const int G = hq / hkv;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t i = 0; i < ns; ++i) {
-        const int g = hs[i] / G;
-        const int nk = lens_s[i] + 1;
-        const uint16_t *Kc = cache_k + ((int64_t)us[i] * hkv + g) * s_cap * d;
-        const uint16_t *Vc = cache_v + ((int64_t)us[i] * hkv + g) * s_cap * d;
-        const uint16_t *qrow = q_rot + i * d;
-        double *acc = (double *)calloc((size_t)d, sizeof(double));
-        double *s = (double *)malloc(sizeof(double) * (size_t)nk);
-        double mx = -INFINITY;
-        for (int j = 0; j < nk; ++j) {
-            double dot = 0.0;
-            for (int e = 0; e < d; ++e)
-                dot += ora_f16_to_f64(qrow[e]) * ora_f16_to_f64(Kc[(int64_t)j * d + e]);
-            s[j] = scale * dot;
-            if (s[j] > mx)
-                mx = s[j];
-        }
-        double denom = 0.0;
-        for (int j = 0; j < nk; ++j) {
-            const double w = exp(s[j] - mx);
-            denom += w;
-            for (int e = 0; e < d; ++e)
-                acc[e] += w * ora_f16_to_f64(Vc[(int64_t)j * d + e]);
-        }
-        for (int e = 0; e < d; ++e)
-            out64[i * d + e] = acc[e] / denom;
-        free(s);
-        free(acc);
-    }
 }
 
 int ora_num_threads(void)

@@ -216,21 +216,6 @@ def test_append_writes_only_its_rows(ora):
         ora.append(ck, cv, k, v, np.array([0, 5, 9], np.int32))
 
 
-def test_decode_rows_sampler_agrees_with_decode(ora):
-    rng = np.random.default_rng(34)
-    n, hq, hkv, d = 3, 8, 2, 128
-    lens = np.array([10, 0, 33], np.int32)
-    q, k, v, pos, ck, cv = _case(rng, n, 1, hq, hkv, d, lens, 40)
-    rp = ora.RopeParams.yarn_tail()
-    out, out64, _ = ora.decode(q[:, 0].copy(), k[:, 0].copy(), v[:, 0].copy(),
-                               pos[:, 0].copy(), ck, cv, lens, 0.0883883, rp)
-    qr, _ = ora.rope(q[:, 0].copy(), pos[:, 0].copy(), rp)
-    us = np.array([0, 2, 1, 2], np.int32)
-    hs = np.array([7, 0, 3, 5], np.int32)
-    got = ora.decode_rows(qr[us, hs], ck, cv, us, hs, lens[us], hq, 0.0883883)
-    np.testing.assert_allclose(got, out64[us, hs], rtol=1e-13, atol=1e-14)
-
-
 def test_capacity_error_is_raised(ora):
     rng = np.random.default_rng(35)
     q, k, v, pos, ck, cv = _case(rng, 1, 4, 2, 1, 8, [0], 4)
@@ -281,3 +266,41 @@ def test_varlen_units_equal_their_own_successive_decodes(ora):
         assert np.isnan(out64[u, new[u]:]).all()
         assert np.array_equal(ck[u][:, lens[u] + new[u]:], ck0[u][:, lens[u] + new[u]:])
     assert np.all(np.isfinite(out64[0])) and np.all(np.isfinite(out64[1, :1]))
+
+
+def test_unit_parameter_sets_equal_separate_calls(ora):
+    # ds4.c study notes, Part 4 sec. 1, Trace 2: each layer has its own frequency base and
+    # scale, and only the compressed layers switch the YaRN ramp on (ext_factor > 0).  A
+    # batch whose units use different parameter sets computes, for every unit, exactly
+    # what a call with that unit's set alone computes: outputs, rotated k and caches.
+    rng = np.random.default_rng(38)
+    n, t, hq, hkv, d = 4, 9, 8, 2, 128
+    plain = ora.RopeParams.plain()
+    compressed = ora.RopeParams(base=160000.0, n_rot=64, yarn=True, freq_scale=1.0 / 16,
+                                ext_factor=1.0, n_ctx_orig=65536, beta_fast=32.0, beta_slow=1.0,
+                                mscale=1.0 + 0.1 * np.log(16.0))
+    sets, unit_set = [plain, compressed], np.array([1, 0, 0, 1], np.int32)
+    lens = [0, 7, 30, 12]
+    q, k, v, pos, ck, cv = _case(rng, n, t, hq, hkv, d, lens, 48)
+    ck_b, cv_b = ck.copy(), cv.copy()
+    out, out64, k64 = ora.prefill_kv(q, k, v, pos, ck_b, cv_b, lens, 0.09, sets, unit_set)
+    for u in range(n):
+        cku, cvu = ck[u:u + 1].copy(), cv[u:u + 1].copy()
+        o, o64, kk = ora.prefill_kv(q[u:u + 1], k[u:u + 1], v[u:u + 1], pos[u:u + 1], cku, cvu,
+                                    lens[u:u + 1], 0.09, sets[unit_set[u]])
+        assert np.array_equal(o[0], out[u]) and np.array_equal(o64[0], out64[u])
+        assert np.array_equal(kk[0], k64[u]) and np.array_equal(cku[0], ck_b[u])
+        assert np.array_equal(cvu[0], cv_b[u])
+    # the two sets really differ on these inputs
+    o_plain, _, _ = ora.prefill_kv(q, k, v, pos, ck.copy(), cv.copy(), lens, 0.09, plain)
+    assert not np.array_equal(o_plain[0], out[0]) and np.array_equal(o_plain[1], out[1])
+    # decode: the same, one step
+    qd, kd, vd = q[:, 0].copy(), k[:, 0].copy(), v[:, 0].copy()
+    dl = np.array(lens, np.int32) + 3
+    ck_b, cv_b = ck.copy(), cv.copy()
+    out, out64, _ = ora.decode(qd, kd, vd, dl, ck_b, cv_b, dl, 0.09, sets, unit_set)
+    for u in range(n):
+        cku, cvu = ck[u:u + 1].copy(), cv[u:u + 1].copy()
+        o, o64, _ = ora.decode(qd[u:u + 1], kd[u:u + 1], vd[u:u + 1], dl[u:u + 1], cku, cvu, dl[u:u + 1],
+                               0.09, sets[unit_set[u]])
+        assert np.array_equal(o64[0], out64[u]) and np.array_equal(cku[0], ck_b[u])

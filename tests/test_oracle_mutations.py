@@ -18,11 +18,10 @@ from tests import test_oracle_codec as C
 from tests import test_oracle_rope as R
 
 MUTANTS = [
-    ("rotation sign", "const double y0 = x0 * c - x1 * s;", "const double y0 = x0 * c + x1 * s;",
-     [R.test_pair_norm_scaled_by_mscale_only, R.test_pair0_turns_by_position_radians_textbook]),
-    ("rotation direction",
-     "const double y0 = x0 * c - x1 * s;\n                const double y1 = x0 * s + x1 * c;",
-     "const double y0 = x0 * c + x1 * s;\n                const double y1 = -x0 * s + x1 * c;",
+    ("rotation sign", "const double complex z = CMPLX(ora_f16_to_f64(x[re_at]), ora_f16_to_f64(x[im_at]));",
+     "const double complex z = CMPLX(ora_f16_to_f64(x[re_at]), -ora_f16_to_f64(x[im_at]));",
+     [R.test_pair0_turns_by_position_radians_textbook, R.test_plain_matches_complex_multiplication]),
+    ("rotation direction", "factor[j] = rp->inverse ? conj(f) : f;", "factor[j] = rp->inverse ? f : conj(f);",
      [R.test_pair0_turns_by_position_radians_textbook, R.test_plain_matches_complex_multiplication]),
     ("frequency exponent", "-2.0 * (double)j / (double)rp->n_rot", "-1.0 * (double)j / (double)rp->n_rot",
      [R.test_frequency_schedule_textbook, R.test_plain_matches_complex_multiplication]),
@@ -33,38 +32,44 @@ MUTANTS = [
     ("YaRN mix swapped", "w = omega * (rp->freq_scale * (1.0 - gamma) + gamma);",
      "w = omega * (rp->freq_scale * gamma + (1.0 - gamma));",
      [R.test_yarn_limits_equal_plain_rotation]),
-    ("mscale dropped", "c = cos(theta) * rp->mscale;", "c = cos(theta);",
+    ("mscale dropped", "f = rp->mscale * CMPLX(cos(theta), sin(theta));", "f = CMPLX(cos(theta), sin(theta));",
      [R.test_pair_norm_scaled_by_mscale_only, R.test_yarn_position_zero_scales_by_mscale]),
-    ("half-split partner adjacent", "const int64_t i1 = i0 + (rp->pairing ? half : 1);",
-     "const int64_t i1 = i0 + (rp->pairing ? 1 : 1);",
+    ("half-split partner adjacent", "const int64_t im_at = rp->pairing ? re_at + half : re_at + 1;",
+     "const int64_t im_at = rp->pairing ? re_at + 1 : re_at + 1;",
      [R.test_half_split_is_adjacent_rotation_of_permuted_dims,
       R.test_half_split_matches_complex_multiplication]),
-    ("half-split pairs from the head start", "const int64_t i0 = base_idx + o + (rp->pairing ? j : 2 * j);",
-     "const int64_t i0 = base_idx + (rp->pairing ? j : o + 2 * j);",
+    ("half-split pairs from the head start", "const int64_t re_at = head + o + (rp->pairing ? j : 2 * j);",
+     "const int64_t re_at = head + (rp->pairing ? j : o + 2 * j);",
      [R.test_half_split_tail_keeps_head_dims]),
-    ("inverse ignored", "const double sin_sign = rp->inverse ? -1.0 : 1.0;", "const double sin_sign = 1.0;",
+    ("inverse ignored", "factor[j] = rp->inverse ? conj(f) : f;", "factor[j] = f;",
      [R.test_inverse_at_pos_is_forward_at_minus_pos, R.test_inverse_undoes_forward_in_fp64]),
-    ("table column shifted", "(double)rp->cos_table[(int64_t)positions[r] * half + j]",
-     "(double)rp->cos_table[(int64_t)positions[r] * half + (j + 1) % half]",
+    ("table column shifted", "(double)rp->cos_table[(int64_t)p * half + j]",
+     "(double)rp->cos_table[(int64_t)p * half + (j + 1) % half]",
      [R.test_table_rotation_closed_form]),
-    ("table rows not by position", "(double)rp->sin_table[(int64_t)positions[r] * half + j]",
-     "(double)rp->sin_table[(int64_t)r % rp->table_rows * half + j]",
+    ("table rows not by position", "(double)rp->sin_table[(int64_t)p * half + j]",
+     "(double)rp->sin_table[(int64_t)(r % rp->table_rows) * half + j]",
      [R.test_table_gather_follows_positions, R.test_table_rotation_closed_form]),
     ("corr dim without 2", "(2.0 * M_PI * beta)", "(M_PI * beta)",
      [R.test_yarn_correction_dims_turn_beta_circles]),
-    ("ramp inverted", "    return 1.0 - y;", "    return y;",
+    ("ramp inverted", "    return 1.0 - along;", "    return along;",
      [R.test_yarn_ramp_endpoints_and_linearity]),
-    ("causal mask off by one", "if (j > lens[u] + tt) {", "if (j >= lens[u] + tt && j > 0) {",
+    ("unit parameter set ignored", "return unit_set ? &sets[unit_set[u]] : &sets[0];", "return &sets[0];",
+     [A.test_unit_parameter_sets_equal_separate_calls]),
+    ("causal mask off by one", "const int nvis = lens[u] + tt + 1;",
+     "const int nvis = lens[u] + tt > 0 ? lens[u] + tt : 1;",
      [A.test_zero_query_gives_prefix_mean, A.test_brute_force_torch_float64]),
-    ("no causal mask", "if (j > lens[u] + tt) {", "if (0) {",
+    ("no causal mask", "const int nvis = lens[u] + tt + 1;", "const int nvis = L;",
      [A.test_zero_query_gives_prefix_mean]),
     ("GQA head mapping", "const int g = h / G;", "const int g = h % hkv;",
      [A.test_brute_force_torch_float64, A.test_single_token_returns_its_value_row]),
-    ("scale dropped", "S[(int64_t)tt * L + j] = scale * acc;", "S[(int64_t)tt * L + j] = acc;",
+    ("scale dropped", "row[j] = (j < nvis) ? scale * row[j] : -INFINITY;",
+     "row[j] = (j < nvis) ? row[j] : -INFINITY;",
      [A.test_brute_force_torch_float64]),
     ("softmax not normalised", "row[j] /= sum;", "row[j] /= 1.0;",
      [A.test_probabilities_sum_to_one]),
     ("decode skips the new key", "const int nk = lens[u] + 1;", "const int nk = lens[u] > 0 ? lens[u] : 1;",
+     [A.test_prefill_equals_successive_decodes]),
+    ("decode scale dropped", "s[j] = scale * s[j];", "s[j] = s[j];",
      [A.test_prefill_equals_successive_decodes]),
     ("append at row 0", "const int64_t dst = (((int64_t)u * hkv + g) * s_cap + lens[u] + tt) * d;",
      "const int64_t dst = (((int64_t)u * hkv + g) * s_cap + tt) * d;",
@@ -74,6 +79,8 @@ MUTANTS = [
     ("f16 decode as bf16-style shift", "v = ldexp((double)(m + 1024), e - 25);",
      "v = ldexp((double)(m + 1024), e - 24);",
      [C.test_decode_every_bit_pattern]),
+    ("score dims out of order", "dot[j] += qi * ki[j];", "dot[j] += qi * ki[(j + 1) % nk];",
+     [A.test_brute_force_torch_float64]),
 ]
 
 
