@@ -183,7 +183,7 @@ def bench_decode(kv, W, name, steps, warmup):
     for i in range(steps):
         flush.sum()
         pa[i].record()
-        kv.probe_stream(inp.cache_k, inp.cache_v, inp.lens, max_len, 1536, sink)
+        probes.stream_rows(inp.cache_k, inp.cache_v, inp.lens, max_len, 1536, sink)
         pb[i].record()
     torch.cuda.synchronize()
     probe_ms = sum(pa[i].elapsed_time(pb[i]) for i in range(steps)) / steps
@@ -200,11 +200,11 @@ def measured_mfma(kv):
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     blocks, iters = 2 * ncu, 4096
     sink = torch.zeros(4 + 4 * blocks, dtype=torch.int64, device="cuda")
-    kv.probe_mfma(blocks, 64, sink)                 # warm-up
+    probes.mfma(blocks, 64, sink)                   # warm-up
     torch.cuda.synchronize()
     e0, e1 = make_events(2)
     e0.record()
-    kv.probe_mfma(blocks, iters, sink)
+    probes.mfma(blocks, iters, sink)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
@@ -307,6 +307,8 @@ def main():
     import torch
     import kv_cache_causal_rope_amd as kv
     from kv_cache_causal_rope_amd import workloads as W
+    global probes
+    from kv_cache_causal_rope_amd import probes
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)

@@ -35,9 +35,11 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
  *     never synchronises.  The caller owns every buffer; the library allocates and frees
  *     no device memory and keeps no per-call state.
- *   - Return value: KVROPE_OK (0) or a negative status.  Every status except
- *     KVROPE_ERR_HIP is decided on the host before any HIP call, so on error nothing has
- *     been launched and no buffer has been touched.  No call clamps silently.
+ *   - Return value: ATTN_OK (0) or a negative status.  Every status except ATTN_ERR_HIP
+ *     is decided on the host before any HIP call, so on error nothing has been launched
+ *     and no buffer has been touched.  No call clamps silently.
+ *   - The library's only state is per thread: the hipError_t of the last failed launch
+ *     (attn_last_hip_error) and the profiling hook (attn_set_profile_events).
  *   - Lengths and positions live in device memory and are not read by the host.  The
  *     host checks the capacity with the caller's bound `max_len` (>= every lens[u]).  A
  *     kernel that finds lens[u] < 0 or lens[u] > max_len writes no cache row of unit u
@@ -54,15 +56,18 @@
 extern "C" {
 #endif
 
-#define KVROPE_OK 0
-#define KVROPE_ERR_NULL (-1)      /* a required pointer is NULL */
-#define KVROPE_ERR_SHAPE (-2)     /* negative size, d != 128, hq % hkv != 0, hkv < 1 */
-#define KVROPE_ERR_ROPE (-3)      /* n_rot odd / < 2 / > d, base <= 1, bad YaRN field */
-#define KVROPE_ERR_CAPACITY (-4)  /* max_len + t > s_cap, or max_len < 0 */
-#define KVROPE_ERR_ALIGN (-5)     /* a tensor pointer is not 16-byte aligned */
-#define KVROPE_ERR_WORKSPACE (-6) /* workspace smaller than kvrope_workspace_size() */
-#define KVROPE_ERR_SCALE (-7)     /* softmax scale not finite or <= 0 */
-#define KVROPE_ERR_HIP (-8)       /* a HIP launch failed (see kvrope_last_hip_error) */
+#define ATTN_OK 0
+#define ATTN_ERR_NULL (-1)      /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE (-2)     /* negative size, d != 128, hq % hkv != 0, hkv < 1 */
+#define ATTN_ERR_ROPE (-3)      /* n_rot odd / < 2 / > d, base <= 1, bad YaRN field, bad set */
+#define ATTN_ERR_CAPACITY (-4)  /* max_len + t > s_cap, or max_len < 0 */
+#define ATTN_ERR_ALIGN (-5)     /* a tensor pointer is not 16-byte aligned */
+#define ATTN_ERR_WORKSPACE (-6) /* workspace smaller than attn_workspace_size() */
+#define ATTN_ERR_SCALE (-7)     /* softmax scale not finite or <= 0 */
+#define ATTN_ERR_HIP (-8)       /* a HIP launch failed (see attn_last_hip_error) */
+
+/* Most rotary parameter sets one call can carry (kvrope_rope_params.n_sets). */
+#define KVROPE_MAX_ROPE_SETS 4
 
 /* Rotary embedding parameters ([ds4] Traces 1-2).
  * Pair j = 0 .. n_rot/2-1 of a head, with o = d - n_rot, is the dims
@@ -99,6 +104,18 @@ typedef struct kvrope_rope_params {
     const float *cos_table; /* NULL, or device float32 [table_rows, n_rot / 2] */
     const float *sin_table; /* NULL exactly when cos_table is */
     int32_t table_rows;     /* >= 1 when the tables are set */
+    /* Per-unit parameter sets ([ds4] Part 4 sec. 1, Trace 2: every layer has its own
+     * frequency base and scale, and only the compressed layers switch the YaRN ramp on).
+     * n_sets = 0: the fields above serve every unit.  1 <= n_sets <= KVROPE_MAX_ROPE_SETS:
+     * unit u takes base, yarn, freq_scale, ext_factor, n_ctx_orig, beta_fast, beta_slow
+     * and mscale from sets[unit_set[u]] (each set is checked like the fields above;
+     * the sets' other fields are not read); n_rot, pairing and inverse stay this
+     * struct's.  Sets and tables exclude each other.  A unit whose device index lies
+     * outside [0, n_sets) gets NaN in its rotated dims (as for a position outside a
+     * table). */
+    int32_t n_sets;
+    const struct kvrope_rope_params *sets; /* host array [n_sets] (read during the call) */
+    const int32_t *unit_set;               /* device int32 [n], 4-byte aligned */
 } kvrope_rope_params;
 
 /* attn_rope_apply -- rotate x in place ([Sophgo] Listings 1-2: top.Rope(x, cos, sin) on
@@ -150,7 +167,7 @@ int attn_prefill_kv(const void *q, const void *k, const void *v, const int32_t *
  * as they were; padding rows of q, k, v and positions may hold anything (they are read
  * but never used).  A unit with new_lens[u] outside [0, t] is treated like an invalid
  * history length: no cache row written, NaN in all t of its out rows.  new_lens may not be
- * NULL (KVROPE_ERR_NULL) unless n * t == 0; everything else as for attn_prefill_kv. */
+ * NULL (ATTN_ERR_NULL) unless n * t == 0; everything else as for attn_prefill_kv. */
 int attn_prefill_kv_varlen(const void *q, const void *k, const void *v, const int32_t *positions,
                            void *history_k, void *history_v, const int32_t *hist_lens, int max_hist,
                            const int32_t *new_lens, void *out, int n, int t, int hq, int hkv, int d,
@@ -160,7 +177,7 @@ int attn_prefill_kv_varlen(const void *q, const void *k, const void *v, const in
  * 6.4.5-6.4.6).
  *   q    [n, 1, hq, d] (= [n, hq, d]);  k, v  [n, 1, hkv, d];  positions [n]
  *   cache_lens  device, int32 [n]: rows already in the cache; max_len >= every one.
- *   workspace   device scratch of at least kvrope_workspace_size(KVROPE_OP_DECODE, n, 1,
+ *   workspace   device scratch of at least attn_workspace_size(ATTN_OP_DECODE, n, 1,
  *               hq, hkv, d, max_len) bytes (may be NULL when that size is 0).  Its
  *               contents on entry do not matter; calls sharing one workspace must be
  *               ordered on one stream.
@@ -202,8 +219,8 @@ int attn_decode(const void *q, const void *k, const void *v, const int32_t *posi
  *   w_o       device, f16 [(w_per_unit ? n : 1), hidden, hq * d]; hidden a multiple of 128
  *   residual  device, f16 [n, t, hidden];  out  device, f16 [n, t, hidden] (may alias
  *             residual)
- * Both are asynchronous on `stream` and return KVROPE_OK, KVROPE_ERR_SHAPE, KVROPE_ERR_NULL,
- * KVROPE_ERR_ALIGN, KVROPE_ERR_CAPACITY / KVROPE_ERR_ROPE (qkv) or KVROPE_ERR_HIP. */
+ * Both are asynchronous on `stream` and return ATTN_OK, ATTN_ERR_SHAPE, ATTN_ERR_NULL,
+ * ATTN_ERR_ALIGN, ATTN_ERR_CAPACITY / ATTN_ERR_ROPE (qkv) or ATTN_ERR_HIP. */
 /* attn_prefill_kv_cached -- attn_prefill_kv whose new k, v rows are already in the caches
  * (written by attn_qkv_project): rows [hist_lens[u], hist_lens[u] + t) of each cache hold
  * the rotated k and the v of the t new tokens; the caches are only read.  q is the
@@ -217,50 +234,24 @@ int attn_qkv_project(const void *x, const void *w_qkv, int w_per_unit, const int
 int attn_out_project(const void *attn, const void *w_o, int w_per_unit, const void *residual, void *out, int n,
                      int t, int hq, int d, int hidden, void *stream);
 
-#define KVROPE_OP_DECODE 1
+#define ATTN_OP_DECODE 1
 
 /* Bytes of device workspace the operation needs (0 for operations that need none). */
-size_t kvrope_workspace_size(int op, int n, int t, int hq, int hkv, int d, int max_len);
+size_t attn_workspace_size(int op, int n, int t, int hq, int hkv, int d, int max_len);
 
 /* Static description of a status code (never NULL). */
-const char *kvrope_status_string(int status);
+const char *attn_status_string(int status);
 
-/* The hipError_t of the most recent KVROPE_ERR_HIP on this thread (0 if none). */
-int kvrope_last_hip_error(void);
+/* The hipError_t of the most recent ATTN_ERR_HIP on the calling thread (0 if none). */
+int attn_last_hip_error(void);
 
-/* Profiling hook.  When `before` / `after` are non-NULL hipEvent_t handles, the next
- * attn_prefill, attn_prefill_kv or attn_decode call records `before` on its stream just
- * before its attention kernel (the flash kernel of prefill, the split-key kernel of
- * decode) and `after` just after that same kernel, then clears the hook.  One hook per
- * process; not thread-safe.  Returns KVROPE_OK. */
-int kvrope_set_profile_events(void *before, void *after);
-
-/* The fp64 -> f16 (nearest, ties to even) conversion the kernels apply to every rotated
- * value, compiled for the host: lets a CPU-only test check it on any input. */
-uint16_t kvrope_f64_to_f16(double x);
-
-/* ---- Measurement helpers (not part of the attention path): the measured ceilings a
- * benchmark reports beside the spec peaks.
- *
- * kvrope_probe_stream -- reads, and only reads, the cache rows a decode step reads:
- * rows [0, lens[u]] of K and V of every (unit, KV head) (cache_k, cache_v, lens laid out
- * as for attn_decode), split into chunks of `chunk` rows (a multiple of 64) per
- * workgroup like the decode kernel, 16-byte lane loads.  Its time is the streaming
- * ceiling of that access pattern.  `sink` (device, >= 4 bytes) is never written in
- * practice.  Requires max_len + 1 <= s_cap; a row past s_cap is never read.
- *
- * kvrope_probe_mfma -- `blocks` workgroups of 4 waves; each wave runs `iters` rounds of
- * four independent v_mfma_f32_32x32x16_f16 chains (32 x 32 x 16 x 2 FLOPs each).
- * sink (device, >= 32 * (blocks + 1) bytes): for workgroup b, sink[4 + 4b .. 4b + 7] as
- * uint64 = real-time counter (100 MHz) at start and end, shader-clock counter at start
- * and end; their ratio gives the clock the matrix cores ran at.
- *
- * Both return KVROPE_OK, KVROPE_ERR_NULL, KVROPE_ERR_SHAPE, KVROPE_ERR_CAPACITY (stream)
- * or KVROPE_ERR_HIP, and are asynchronous on `stream`. */
-int kvrope_probe_stream(const void *cache_k, const void *cache_v, const int32_t *lens, int n,
-                        int hkv, int s_cap, int d, int max_len, int chunk, void *sink,
-                        void *stream);
-int kvrope_probe_mfma(int blocks, int iters, void *sink, void *stream);
+/* Profiling hook of the calling thread.  When `before` / `after` are non-NULL hipEvent_t
+ * handles, the next attn_prefill, attn_prefill_kv, attn_prefill_kv_varlen,
+ * attn_prefill_kv_cached or attn_decode call made ON THIS THREAD records `before` on its
+ * stream just before its attention kernel (the flash kernel of prefill, the split-key
+ * kernel of decode) and `after` just after that same kernel, then clears the hook.  Calls
+ * on other threads neither see nor clear it.  Returns ATTN_OK. */
+int attn_set_profile_events(void *before, void *after);
 
 #ifdef __cplusplus
 }

@@ -24,22 +24,22 @@ import torch  # imported first: the library binds to the HIP runtime torch has l
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvrope.so")
 
-KVROPE_OK = 0
-KVROPE_ERR_NULL = -1
-KVROPE_ERR_SHAPE = -2
-KVROPE_ERR_ROPE = -3
-KVROPE_ERR_CAPACITY = -4
-KVROPE_ERR_ALIGN = -5
-KVROPE_ERR_WORKSPACE = -6
-KVROPE_ERR_SCALE = -7
-KVROPE_ERR_HIP = -8
-KVROPE_OP_DECODE = 1
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_SHAPE = -2
+ATTN_ERR_ROPE = -3
+ATTN_ERR_CAPACITY = -4
+ATTN_ERR_ALIGN = -5
+ATTN_ERR_WORKSPACE = -6
+ATTN_ERR_SCALE = -7
+ATTN_ERR_HIP = -8
+ATTN_OP_DECODE = 1
+MAX_ROPE_SETS = 4
 
 # every symbol include/kvrope.h declares
 EXPORTS = ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
-           "attn_prefill_kv_varlen", "attn_decode", "kvrope_workspace_size", "kvrope_status_string",
-           "kvrope_last_hip_error", "kvrope_set_profile_events", "kvrope_f64_to_f16",
-           "kvrope_probe_stream", "kvrope_probe_mfma", "attn_qkv_project", "attn_out_project",
+           "attn_prefill_kv_varlen", "attn_decode", "attn_workspace_size", "attn_status_string",
+           "attn_last_hip_error", "attn_set_profile_events", "attn_qkv_project", "attn_out_project",
            "attn_prefill_kv_cached"]
 
 
@@ -54,52 +54,82 @@ class RopeParams(ctypes.Structure):
 
     ``with_variant`` sets the half-split pairing, the inverse rotation and the caller's
     cos / sin tables (CUDA float32 tensors [rows, n_rot / 2]; the struct keeps them alive).
+    ``with_sets`` gives each unit its own frequency parameters.
     """
-    _fields_ = [("base", ctypes.c_double), ("n_rot", ctypes.c_int32), ("yarn", ctypes.c_int32),
-                ("freq_scale", ctypes.c_double), ("ext_factor", ctypes.c_double),
-                ("n_ctx_orig", ctypes.c_int32), ("beta_fast", ctypes.c_double),
-                ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double),
-                ("pairing", ctypes.c_int32), ("inverse", ctypes.c_int32),
-                ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
-                ("table_rows", ctypes.c_int32)]
 
-    @classmethod
-    def plain(cls, n_rot: int = 128, base: float = 10000.0) -> "RopeParams":
-        return cls(base, n_rot, 0, 1.0, 0.0, 4096, 32.0, 1.0, 1.0)
 
-    def with_variant(self, half_split: bool = False, inverse: bool = False, cos_table=None,
-                     sin_table=None) -> "RopeParams":
-        """A copy with the given pairing, direction and tables."""
-        r = RopeParams.from_buffer_copy(self)
-        r.pairing, r.inverse = int(half_split), int(inverse)
-        if (cos_table is None) != (sin_table is None):
-            raise ValueError("cos_table and sin_table go together")
-        if cos_table is not None:
-            for tt in (cos_table, sin_table):
-                if not (tt.is_cuda and tt.dtype == torch.float32 and tt.is_contiguous() and tt.dim() == 2
-                        and tt.shape == cos_table.shape and tt.shape[1] == self.n_rot // 2):
-                    raise ValueError("tables must be contiguous CUDA float32 [rows, n_rot / 2]")
-            r.cos_table, r.sin_table = cos_table.data_ptr(), sin_table.data_ptr()
-            r.table_rows = cos_table.shape[0]
-            r._keep = (cos_table, sin_table)
-        else:
-            r.cos_table = r.sin_table = None
-            r.table_rows = 0
-        return r
+RopeParams._fields_ = [("base", ctypes.c_double), ("n_rot", ctypes.c_int32), ("yarn", ctypes.c_int32),
+                       ("freq_scale", ctypes.c_double), ("ext_factor", ctypes.c_double),
+                       ("n_ctx_orig", ctypes.c_int32), ("beta_fast", ctypes.c_double),
+                       ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double),
+                       ("pairing", ctypes.c_int32), ("inverse", ctypes.c_int32),
+                       ("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                       ("table_rows", ctypes.c_int32), ("n_sets", ctypes.c_int32),
+                       ("sets", ctypes.POINTER(RopeParams)), ("unit_set", ctypes.c_void_p)]
 
-    @classmethod
-    def yarn_tail(cls, n_rot: int = 64, base: float = 10000.0, factor: float = 4.0,
-                  n_ctx_orig: int = 4096, beta_fast: float = 32.0, beta_slow: float = 1.0,
-                  mscale: Optional[float] = None) -> "RopeParams":
-        if mscale is None:
-            mscale = 1.0 + 0.1 * math.log(factor)
-        return cls(base, n_rot, 1, 1.0 / factor, 1.0, n_ctx_orig, beta_fast, beta_slow, mscale)
 
-    @classmethod
-    def from_fields(cls, r) -> "RopeParams":
-        """From any object with the same field names (e.g. a workload's Rope)."""
-        return cls(r.base, r.n_rot, int(r.yarn), r.freq_scale, r.ext_factor, r.n_ctx_orig,
-                   r.beta_fast, r.beta_slow, r.mscale)
+def _plain(cls, n_rot: int = 128, base: float = 10000.0) -> "RopeParams":
+    return cls(base, n_rot, 0, 1.0, 0.0, 4096, 32.0, 1.0, 1.0)
+
+
+def _with_variant(self, half_split: bool = False, inverse: bool = False, cos_table=None,
+                  sin_table=None) -> "RopeParams":
+    """A copy with the given pairing, direction and tables."""
+    r = RopeParams.from_buffer_copy(self)
+    r.pairing, r.inverse = int(half_split), int(inverse)
+    if (cos_table is None) != (sin_table is None):
+        raise ValueError("cos_table and sin_table go together")
+    if cos_table is not None:
+        for tt in (cos_table, sin_table):
+            if not (tt.is_cuda and tt.dtype == torch.float32 and tt.is_contiguous() and tt.dim() == 2
+                    and tt.shape == cos_table.shape and tt.shape[1] == self.n_rot // 2):
+                raise ValueError("tables must be contiguous CUDA float32 [rows, n_rot / 2]")
+        r.cos_table, r.sin_table = cos_table.data_ptr(), sin_table.data_ptr()
+        r.table_rows = cos_table.shape[0]
+        r._keep = (cos_table, sin_table)
+    else:
+        r.cos_table = r.sin_table = None
+        r.table_rows = 0
+    r.n_sets, r.sets, r.unit_set = 0, None, None
+    return r
+
+
+def _with_sets(self, sets, unit_set: torch.Tensor) -> "RopeParams":
+    """A copy whose unit u takes its frequency fields (base, YaRN fields, mscale) from
+    sets[unit_set[u]] (1 <= len(sets) <= MAX_ROPE_SETS; unit_set a CUDA int32 [n] tensor);
+    n_rot, pairing and inverse stay this struct's."""
+    sets = list(sets)
+    if not (isinstance(unit_set, torch.Tensor) and unit_set.is_cuda and unit_set.dtype == torch.int32
+            and unit_set.is_contiguous() and unit_set.dim() == 1):
+        raise ValueError("unit_set must be a contiguous CUDA int32 [n] tensor")
+    arr = (RopeParams * len(sets))(*[RopeParams.from_buffer_copy(x) for x in sets])
+    r = RopeParams.from_buffer_copy(self)
+    r.n_sets = len(sets)
+    r.sets = ctypes.cast(arr, ctypes.POINTER(RopeParams))
+    r.unit_set = unit_set.data_ptr()
+    r._keep = (arr, unit_set, getattr(self, "_keep", None))
+    return r
+
+
+def _yarn_tail(cls, n_rot: int = 64, base: float = 10000.0, factor: float = 4.0,
+               n_ctx_orig: int = 4096, beta_fast: float = 32.0, beta_slow: float = 1.0,
+               mscale: Optional[float] = None) -> "RopeParams":
+    if mscale is None:
+        mscale = 1.0 + 0.1 * math.log(factor)
+    return cls(base, n_rot, 1, 1.0 / factor, 1.0, n_ctx_orig, beta_fast, beta_slow, mscale)
+
+
+def _from_fields(cls, r) -> "RopeParams":
+    """From any object with the same field names (e.g. a workload's Rope)."""
+    return cls(r.base, r.n_rot, int(r.yarn), r.freq_scale, r.ext_factor, r.n_ctx_orig,
+               r.beta_fast, r.beta_slow, r.mscale)
+
+
+RopeParams.plain = classmethod(_plain)
+RopeParams.with_variant = _with_variant
+RopeParams.with_sets = _with_sets
+RopeParams.yarn_tail = classmethod(_yarn_tail)
+RopeParams.from_fields = classmethod(_from_fields)
 
 
 _lib = None
@@ -137,36 +167,32 @@ def lib() -> ctypes.CDLL:
                                          [ctypes.c_double, rp, _P])
     L.attn_decode.argtypes = ([_P] * 7 + [_I, _P] + [_I] * 5 +
                               [ctypes.c_double, rp, _P, ctypes.c_size_t, _P])
-    L.kvrope_workspace_size.argtypes = [_I] * 7
-    L.kvrope_workspace_size.restype = ctypes.c_size_t
-    L.kvrope_status_string.argtypes = [_I]
-    L.kvrope_status_string.restype = ctypes.c_char_p
-    L.kvrope_last_hip_error.restype = _I
-    L.kvrope_set_profile_events.argtypes = [_P, _P]
-    L.kvrope_f64_to_f16.argtypes = [ctypes.c_double]
-    L.kvrope_f64_to_f16.restype = ctypes.c_uint16
-    L.kvrope_probe_stream.argtypes = [_P, _P, _P] + [_I] * 6 + [_P, _P]
-    L.kvrope_probe_mfma.argtypes = [_I, _I, _P, _P]
+    L.attn_workspace_size.argtypes = [_I] * 7
+    L.attn_workspace_size.restype = ctypes.c_size_t
+    L.attn_status_string.argtypes = [_I]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_hip_error.restype = _I
+    L.attn_set_profile_events.argtypes = [_P, _P]
     L.attn_qkv_project.argtypes = [_P, _P, _I, _P, _P, _P, _P, _P] + [_I] * 8 + [rp, _P]
     L.attn_out_project.argtypes = [_P, _P, _I, _P, _P] + [_I] * 5 + [_P]
     L.attn_prefill_kv_cached.argtypes = [_P] * 5 + [_I, _P] + [_I] * 6 + [ctypes.c_double, rp, _P]
     for rtn in ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
-                "attn_prefill_kv_varlen", "attn_decode", "kvrope_set_profile_events", "kvrope_probe_stream",
-                "kvrope_probe_mfma", "attn_qkv_project", "attn_out_project", "attn_prefill_kv_cached"]:
+                "attn_prefill_kv_varlen", "attn_decode", "attn_set_profile_events", "attn_qkv_project",
+                "attn_out_project", "attn_prefill_kv_cached"]:
         getattr(L, rtn).restype = _I
     _lib = L
     return L
 
 
 def status_string(status: int) -> str:
-    return lib().kvrope_status_string(status).decode()
+    return lib().attn_status_string(status).decode()
 
 
 def _check(status: int) -> None:
-    if status != KVROPE_OK:
+    if status != ATTN_OK:
         msg = status_string(status)
-        if status == KVROPE_ERR_HIP:
-            msg += f" (hipError {lib().kvrope_last_hip_error()})"
+        if status == ATTN_ERR_HIP:
+            msg += f" (hipError {lib().attn_last_hip_error()})"
         raise KVRopeError(status, msg)
 
 
@@ -198,38 +224,26 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _alloc(stream, make):
+    """Allocate with `make()` in the caching allocator's pool of the stream the kernels run
+    on, so that torch does not hand the memory to other work while those kernels may still
+    use it."""
+    if stream is None:
+        return make()
+    with torch.cuda.stream(stream):
+        return make()
+
+
 def workspace_size(n: int, hq: int, hkv: int, max_len: int, d: int = 128) -> int:
-    return int(lib().kvrope_workspace_size(KVROPE_OP_DECODE, n, 1, hq, hkv, d, max_len))
+    return int(lib().attn_workspace_size(ATTN_OP_DECODE, n, 1, hq, hkv, d, max_len))
 
 
 def set_profile_events(before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]):
-    """Record `before` / `after` around the attention kernel of the next prefill / decode
-    call (events must have been created on the current device)."""
+    """Record `before` / `after` around the attention kernel of the calling thread's next
+    prefill / decode call (events must have been created on the current device)."""
     b = ctypes.c_void_p(before.cuda_event) if before is not None else None
     a = ctypes.c_void_p(after.cuda_event) if after is not None else None
-    _check(lib().kvrope_set_profile_events(b, a))
-
-
-def f64_to_f16_bits(x: float) -> int:
-    """The kernels' fp64 -> f16 conversion, run on the host (for tests)."""
-    return int(lib().kvrope_f64_to_f16(float(x)))
-
-
-def probe_stream(cache_k, cache_v, lens, max_len: int, chunk: int, sink, stream=None):
-    """Read (only) rows [0, lens[u]] of every (unit, KV head) of the caches, in chunks of
-    `chunk` rows per workgroup: the streaming ceiling of a decode step's reads."""
-    n, hkv, s_cap, d = cache_k.shape
-    _f16("cache_k", cache_k, (n, hkv, s_cap, d))
-    _f16("cache_v", cache_v, (n, hkv, s_cap, d))
-    _i32("lens", lens, (n,))
-    _check(lib().kvrope_probe_stream(_ptr(cache_k), _ptr(cache_v), _ptr(lens), n, hkv, s_cap, d,
-                                     int(max_len), int(chunk), _ptr(sink), _stream(stream)))
-
-
-def probe_mfma(blocks: int, iters: int, sink, stream=None):
-    """`blocks` workgroups x 4 waves, each `iters` rounds of 4 independent f16 MFMAs
-    (32x32x16); sink (uint64) gets per-workgroup clock counters at [4 + 4b, 8 + 4b)."""
-    _check(lib().kvrope_probe_mfma(int(blocks), int(iters), _ptr(sink), _stream(stream)))
+    _check(lib().attn_set_profile_events(b, a))
 
 
 def rope_apply(x: torch.Tensor, positions: torch.Tensor, rope: RopeParams, stream=None):
@@ -273,7 +287,7 @@ def prefill(q, k, v, positions, cache_k, cache_v, rope: RopeParams, scale: Optio
     n, t, hq, hkv, d, s_cap = _attn_shapes(q, k, v, cache_k, cache_v)
     _i32("positions", positions, (n, t))
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(stream, lambda: torch.empty_like(q))
     _f16("out", out, q.shape)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(cache_k),
@@ -290,7 +304,7 @@ def prefill_kv(q, k, v, positions, cache_k, cache_v, hist_lens, max_hist: int, r
     _i32("positions", positions, (n, t))
     _i32("hist_lens", hist_lens, (n,))
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(stream, lambda: torch.empty_like(q))
     _f16("out", out, q.shape)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().attn_prefill_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(cache_k),
@@ -310,7 +324,7 @@ def prefill_kv_varlen(q, k, v, positions, cache_k, cache_v, hist_lens, new_lens,
     _i32("hist_lens", hist_lens, (n,))
     _i32("new_lens", new_lens, (n,))
     if out is None:
-        out = torch.zeros_like(q)
+        out = _alloc(stream, lambda: torch.zeros_like(q))
     _f16("out", out, q.shape)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().attn_prefill_kv_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(cache_k),
@@ -345,7 +359,7 @@ def qkv_project(x, w_qkv, positions, cache_k, cache_v, lens, max_len: int, rope:
     if lens is not None:
         _i32("lens", lens, (n,))
     if q_out is None:
-        q_out = torch.empty((n, t, hq, d), dtype=torch.float16, device=x.device)
+        q_out = _alloc(stream, lambda: torch.empty((n, t, hq, d), dtype=torch.float16, device=x.device))
     _f16("q_out", q_out, (n, t, hq, d))
     _check(lib().attn_qkv_project(_ptr(x), _ptr(w_qkv), per_unit, _ptr(positions), _ptr(q_out),
                                   _ptr(cache_k), _ptr(cache_v), _ptr(lens) if lens is not None else None,
@@ -367,7 +381,7 @@ def prefill_kv_cached(q, positions, cache_k, cache_v, hist_lens, max_hist: int, 
     if hist_lens is not None:
         _i32("hist_lens", hist_lens, (n,))
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(stream, lambda: torch.empty_like(q))
     _f16("out", out, q.shape)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     _check(lib().attn_prefill_kv_cached(_ptr(q), _ptr(positions), _ptr(cache_k), _ptr(cache_v),
@@ -390,7 +404,7 @@ def out_project(attn, w_o, residual, out: Optional[torch.Tensor] = None, stream=
     _f16("residual", residual, (n, t, hidden))
     per_unit = _weights(w_o, n, hidden, hq * d, "w_o")
     if out is None:
-        out = torch.empty_like(residual)
+        out = _alloc(stream, lambda: torch.empty_like(residual))
     _f16("out", out, (n, t, hidden))
     _check(lib().attn_out_project(_ptr(attn), _ptr(w_o), per_unit, _ptr(residual), _ptr(out), n, t, hq, d,
                                   hidden, _stream(stream)))
@@ -415,11 +429,11 @@ def decode(q, k, v, positions, cache_k, cache_v, lens, max_len: int, rope: RopeP
     _i32("positions", positions, (n,))
     _i32("lens", lens, (n,))
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(stream, lambda: torch.empty_like(q))
     _f16("out", out, q.shape)
     need = workspace_size(n, hq, hkv, max_len, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _alloc(stream, lambda: torch.empty(max(need, 16), dtype=torch.uint8, device=q.device))
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous uint8 CUDA tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else scale

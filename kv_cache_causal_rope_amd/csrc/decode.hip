@@ -4,7 +4,7 @@
 // One decode step per unit u (Sophgo MLIR-based LLM compilation paper, sec. 4.1: query
 // length 1, keys = every earlier token; Buddy-MLIR walkthrough, sec. 6.4.5-6.4.6: the new
 // token sits at position = current cache length):
-//   1. q[u] and k[u] are rotated at positions[u] (fp64 trig, rounded once to f16 --
+//   1. q[u] and k[u] are rotated at positions[u] (fp64 factors, rounded once to f16 --
 //      "ds4.c study notes", Part 4 sec. 1, Trace 2);
 //   2. the rotated k and the raw v are written to cache row lens[u];
 //   3. each query head h attends over rows 0 .. lens[u] of KV head h / (hq / hkv)
@@ -26,6 +26,7 @@
 // deterministic.  No float atomics anywhere.
 #include "device_common.h"
 #include "launch.h"
+#include "rope_device.h"
 
 #include <math.h>
 
@@ -108,20 +109,15 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p, RopeT
     const int k1 = min(k0 + p.chunk, nk);
     const bool has_new = (len >= k0 && len < k1);
 
-    // ---- prologue: trig once per pair (fp64), shared by q heads and k (or the caller's
-    // table entries of the token's position; NaN when the table does not cover it)
+    // ---- prologue: the factors of each rotated pair once (fp64), shared by the q heads
+    // and k, by the routine every kernel that writes K rows uses (or the caller's table
+    // entries of the token's position; NaN when the table does not cover it)
     const int posi = p.pos[u];
     if (tid < tab.n_pairs) {
-        double s, co;
-        if (tab.cos_t) {
-            const bool in = posi >= 0 && posi < tab.rows;
-            co = in ? (double)tab.cos_t[(int64_t)posi * tab.n_pairs + tid] : __builtin_nan("");
-            s = in ? (double)tab.sin_t[(int64_t)posi * tab.n_pairs + tid] : __builtin_nan("");
-        } else {
-            sincos((double)posi * tab.w[tid], &s, &co);
-        }
-        sm.cs[tid] = co * tab.mscale;
-        sm.sn[tid] = s * tab.mscale * tab.sgn;
+        double co, s;
+        pair_factor(tid, posi, tab, rope_set(tab, u), co, s);
+        sm.cs[tid] = co;
+        sm.sn[tid] = s;
     }
     __syncthreads();
     {

@@ -19,23 +19,35 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxPairs = kHeadDim / 2;
+constexpr int kMaxRopeSets = 4; // KVROPE_MAX_ROPE_SETS
 
 // Per-call rotary table, passed by value as a kernel argument.  Built on the host in
-// fp64 (rope_table() in api.cpp): pair j of a head rotates dims (off + 2j, off + 2j + 1)
-// by theta = pos * w[j]; wrev[j] = w[j] / (2 pi) serves the fp32 path that works in
-// revolutions.
+// fp64 (rope_table() in api.hip): pair j of a head rotates dims (off + 2j, off + 2j + 1)
+// by 2 pi * pos * wrev[s][j] radians (wrev: revolutions per position) and scales them
+// by mscale[s], where s is the unit's parameter set.
 struct RopeTable {
-    double w[kMaxPairs];
-    double wrev[kMaxPairs];
-    double mscale;
+    double wrev[kMaxRopeSets][kMaxPairs];
+    double mscale[kMaxRopeSets];
+    const int32_t *unit_set; // device [n]: set of unit u (NULL: set 0 for every unit)
+    int nsets;
     int n_pairs; // n_rot / 2
     int off;     // first rotated dim (d - n_rot)
     int half;    // 1: pair j is dims (off + j, off + j + n_pairs); 0: (off + 2j, off + 2j + 1)
     double sgn;  // sign of the sine: -1 for the inverse rotation
-    const float *cos_t; // caller tables [rows][n_pairs] (NULL: cos / sin of pos * w)
+    const float *cos_t; // caller tables [rows][n_pairs] (NULL: cos / sin of the angle)
     const float *sin_t;
     int rows;
 };
+
+// The parameter set of unit u, or -1 when the caller's index lies outside [0, nsets)
+// (its rotated dims become NaN, like a position a table does not cover).
+__device__ inline int rope_set(const RopeTable &tab, int u)
+{
+    if (!tab.unit_set)
+        return 0;
+    const int s = tab.unit_set[u];
+    return (s >= 0 && s < tab.nsets) ? s : -1;
+}
 
 // fp64 -> IEEE binary16, round to nearest, ties to even, by bit manipulation.
 // Used for every rotated K value, so the cache holds the correctly rounded f16 of the

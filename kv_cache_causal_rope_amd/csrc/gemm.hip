@@ -226,6 +226,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmParams p, RopeTable tab)
             return;
         const int g = hn - p.hq;
         const int first = tab.off >> 3, h8 = tab.n_pairs >> 3;
+        const int set = rope_set(tab, u);
         for (int it = tid; it < TM * 16; it += NTHR) {
             const int row = it >> 4, ch = it & 15;
             if (row >= rows)
@@ -241,13 +242,13 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmParams p, RopeTable tab)
                 } else if (ch < first + h8) {
                     Chunk16 bb, yb;
                     chunk_f16(row, ch + h8, bb.h);
-                    rotate_half_chunks(a.h, bb.h, y.h, yb.h, 8 * (ch - first), pos, tab);
+                    rotate_half_chunks(a.h, bb.h, y.h, yb.h, 8 * (ch - first), pos, tab, set);
                     reinterpret_cast<uint4 *>(dst)[ch] = y.v;
                     reinterpret_cast<uint4 *>(dst)[ch + h8] = yb.v;
                 }
             } else if (8 * ch + 7 >= tab.off) {
                 double cs[4], sn[4];
-                chunk_trig(ch, pos, tab, cs, sn);
+                chunk_trig(ch, pos, tab, set, cs, sn);
                 rotate_chunk_f64(a.h, y.h, ch, cs, sn, tab.off);
                 reinterpret_cast<uint4 *>(dst)[ch] = y.v;
             } else {

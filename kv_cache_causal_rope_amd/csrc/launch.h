@@ -10,7 +10,8 @@ namespace kvrope {
 
 struct RopeTable;
 
-hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int h,
+// rows = units x t (row r belongs to unit r / t, whose parameter set it rotates with)
+hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int t, int h,
                                const RopeTable &tab, hipStream_t stream);
 
 hipError_t launch_append(uint16_t *cache_k, uint16_t *cache_v, const uint16_t *k,

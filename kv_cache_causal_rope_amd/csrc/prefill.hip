@@ -480,8 +480,10 @@ template <int H16, bool TAB>
 __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab, QRot rot)
 {
     __shared__ __align__(16) char lds[2 * NSTAGE * TILE_B];
-    __shared__ double wdim[kMaxPairs]; // revolutions per position of dim pair dp (0: unrotated)
-    __shared__ float sdim[kMaxPairs];  // output scale of dim pair dp
+    // per parameter set (row kMaxRopeSets: NaN, for an invalid set index): revolutions per
+    // position of dim pair dp (0: unrotated) and its output scale
+    __shared__ double wdim[kMaxRopeSets + 1][kMaxPairs];
+    __shared__ float sdim[kMaxRopeSets + 1][kMaxPairs];
     __shared__ int ovf_unit;           // last unit whose row sums overflowed
 
     const int tid = threadIdx.x;
@@ -499,12 +501,18 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     // of 8 too, every unit of a pair runs on the same XCD and its K/V stays in that L2.
     const int P = gridDim.x;
 
-    // rotation tables, shared by every unit
-    if (tid < kMaxPairs) {
-        const bool rot_t = 2 * tid >= tab.off;
+    // rotation tables of every parameter set, shared by every unit
+    if (tid < (kMaxRopeSets + 1) * kMaxPairs) {
+        const int rs = tid / kMaxPairs, dp = tid % kMaxPairs;
+        const bool rot_t = 2 * dp >= tab.off;
         const float sl2 = p.scale_log2;
-        wdim[tid] = rot_t ? tab.sgn * tab.wrev[tid - (tab.off >> 1)] : 0.0;
-        sdim[tid] = rot_t ? (float)tab.mscale * sl2 : sl2;
+        if (rs < tab.nsets) {
+            wdim[rs][dp] = rot_t ? tab.sgn * tab.wrev[rs][dp - (tab.off >> 1)] : 0.0;
+            sdim[rs][dp] = rot_t ? (float)tab.mscale[rs] * sl2 : sl2;
+        } else {
+            wdim[rs][dp] = __builtin_nan("");
+            sdim[rs][dp] = __builtin_nanf("");
+        }
     }
     if (tid == 0)
         ovf_unit = -1;
@@ -531,6 +539,9 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const int i = i0 + c;
         const int hist = p.lens ? p.lens[u] : 0;
         const int tu = p.new_lens ? p.new_lens[u] : p.t; // this unit's new tokens
+        const int rset = rope_set(tab, u);
+        const double *wd = wdim[rset < 0 ? kMaxRopeSets : rset];
+        const float *sd = sdim[rset < 0 ? kMaxRopeSets : rset];
         if (hist < 0 || hist > p.max_hist || tu < 0 || tu > p.t) {
             // invalid history or new-token count: no cache was written for this unit; report
             // NaN in every row
@@ -625,11 +636,11 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         half8 qop[8];
         if (ntok <= 2 * QB) {
             wg_barrier(); // every wave has read its previous unit's output rows back
-            fill_rot_table<TAB>(lds, tpos, ntok, tid, wdim, sdim, rot);
+            fill_rot_table<TAB>(lds, tpos, ntok, tid, wd, sd, rot);
             wg_barrier();
             rotate_q_tab_t<H16>(qop, qin, lds, ntok, (tb - tb_first) * QB + c, hh);
         } else {
-            rotate_q_t<H16, TAB>(qop, qin, qpos, hh, wdim, sdim, rot);
+            rotate_q_t<H16, TAB>(qop, qin, qpos, hh, wd, sd, rot);
         }
 
         // ---- per-lane LDS byte addresses (stage 0; other stages by immediate offsets)
@@ -878,7 +889,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         wg_barrier();
         if (ovf_unit == v) {
             // (without tables the rotation needs nothing beyond LDS: no live kernel arguments)
-            exact_unit<H16, TAB>(p, lds, wdim, sdim, u, g, wk, hist, tu, TAB ? rot : QRot{});
+            exact_unit<H16, TAB>(p, lds, wd, sd, u, g, wk, hist, tu, TAB ? rot : QRot{});
             continue;
         }
 

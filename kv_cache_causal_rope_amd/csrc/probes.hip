@@ -1,14 +1,15 @@
-// probes.hip -- measured ceilings that the benchmark reports beside the spec peaks
-// (gfx950): a read-only stream over exactly the cache rows a decode step reads, with the
-// decode kernel's own (unit, KV head, key chunk) decomposition, and an f16 MFMA
-// microbenchmark that also records the shader clock it ran at.
+// probes.hip -- libkvrope_probes.so: measured ceilings that the benchmark reports beside
+// the spec peaks (gfx950), declared in include/kvrope_probes.h: a plain front-to-back read
+// of a large buffer, a read-only stream over exactly the cache rows a decode step reads,
+// and an f16 MFMA microbenchmark that also records the shader clock it ran at.
 //
-// Both kernels compute nothing that is used: every lane folds what it read (or its
+// The kernels compute nothing that is used: every lane folds what it read (or its
 // accumulators) into one word and writes it only when it equals a value no input
 // produces in practice, so the loads and MFMAs cannot be optimised away while the
 // writes cost nothing.
 #include "device_common.h"
 #include "kvrope.h"
+#include "kvrope_probes.h"
 
 #include <stdint.h>
 
@@ -17,6 +18,30 @@ namespace kvrope {
 namespace {
 
 constexpr uint32_t kNever = 0x7f3a91c5u;
+
+// Grid-stride read of n16 16-byte words: workgroup b takes words
+// [32 KB-block b, b + gridDim, ...); in a block, load x of thread t reads word
+// 256 x + t, so each load instruction of a wave covers 1 KB contiguous.
+__global__ void __launch_bounds__(256) read_kernel(const u32x4 *__restrict__ buf, size_t n16,
+                                                   uint32_t *__restrict__ sink)
+{
+    constexpr int U = 8;
+    const size_t step = (size_t)gridDim.x * 256 * U;
+    uint32_t acc = 0;
+    for (size_t i0 = (size_t)blockIdx.x * 256 * U + threadIdx.x; i0 < n16; i0 += step) {
+        u32x4 a[U];
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            const size_t i = i0 + 256 * (size_t)x;
+            a[x] = i < n16 ? buf[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int x = 0; x < U; ++x)
+            acc ^= a[x][0] ^ a[x][1] ^ a[x][2] ^ a[x][3];
+    }
+    if (acc == kNever)
+        sink[0] = acc;
+}
 
 // One workgroup per (unit, KV head, chunk of `chunk` rows), 256 threads; rows
 // [0, lens[u]] of K and V (the cache rows of a decode step with the new row appended).
@@ -99,37 +124,53 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, uint32_t see
 
 extern "C" {
 
-int kvrope_probe_stream(const void *cache_k, const void *cache_v, const int32_t *lens, int n,
-                        int hkv, int s_cap, int d, int max_len, int chunk, void *sink, void *stream)
+int kvprobe_read(const void *buf, size_t bytes, int blocks, void *sink, void *stream)
+{
+    if (!buf || !sink)
+        return ATTN_ERR_NULL;
+    if (bytes % 16 != 0 || blocks < 1 || (reinterpret_cast<uintptr_t>(buf) & 15u))
+        return ATTN_ERR_SHAPE;
+    if (bytes == 0)
+        return ATTN_OK;
+    hipLaunchKernelGGL(kvrope::read_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), static_cast<const kvrope::u32x4 *>(buf),
+                       bytes / 16, static_cast<uint32_t *>(sink));
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int kvprobe_stream(const void *cache_k, const void *cache_v, const int32_t *lens, int n, int hkv,
+                   int s_cap, int d, int max_len, int chunk, void *sink, void *stream)
 {
     if (!cache_k || !cache_v || !lens || !sink)
-        return KVROPE_ERR_NULL;
-    if (n < 0 || hkv < 1 || s_cap < 1 || d != kvrope::kHeadDim || chunk < 64 || chunk % 64 != 0)
-        return KVROPE_ERR_SHAPE;
+        return ATTN_ERR_NULL;
+    if (n < 0 || hkv < 1 || s_cap < 1 || d != kvrope::kHeadDim || chunk < 32 || chunk % 32 != 0)
+        return ATTN_ERR_SHAPE;
     if (max_len < 0 || max_len + 1 > s_cap)
-        return KVROPE_ERR_CAPACITY;
+        return ATTN_ERR_CAPACITY;
     if (n == 0)
-        return KVROPE_OK;
+        return ATTN_OK;
     const int nsplit = (max_len + 1 + chunk - 1) / chunk;
     const int64_t blocks = (int64_t)n * hkv * nsplit;
     if (blocks > 0x7fffffff)
-        return KVROPE_ERR_SHAPE;
+        return ATTN_ERR_SHAPE;
     hipLaunchKernelGGL(kvrope::stream_rows_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t *>(cache_k),
                        static_cast<const uint16_t *>(cache_v), lens, hkv, s_cap, chunk, nsplit,
                        static_cast<uint32_t *>(sink));
-    return hipGetLastError() == hipSuccess ? KVROPE_OK : KVROPE_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int kvrope_probe_mfma(int blocks, int iters, void *sink, void *stream)
+int kvprobe_mfma(int blocks, int iters, void *sink, void *stream)
 {
     if (!sink)
-        return KVROPE_ERR_NULL;
+        return ATTN_ERR_NULL;
     if (blocks < 1 || iters < 1)
-        return KVROPE_ERR_SHAPE;
+        return ATTN_ERR_SHAPE;
     hipLaunchKernelGGL(kvrope::mfma_probe_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), iters, 12345u, static_cast<uint64_t *>(sink));
-    return hipGetLastError() == hipSuccess ? KVROPE_OK : KVROPE_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
+
+uint16_t kvprobe_f64_to_f16(double x) { return kvrope::f64_to_f16_rne(x); }
 
 } // extern "C"

@@ -3,7 +3,9 @@
 // Rotation ("ds4.c study notes", Part 4 sec. 1, Trace 2): pair j of a head holds dims
 // (off + 2j, off + 2j + 1), off = d - n_rot (or, half-split, (off + j, off + j + n_rot/2));
 // with theta = pos * w[j], c = cos(theta) * mscale and s = sgn * sin(theta) * mscale
-// (sgn = -1 for the inverse rotation) the pair (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c).
+// (sgn = -1 for the inverse rotation) the pair (x0, x1) becomes (x0 c - x1 s, x0 s + x1 c);
+// w and mscale are those of the unit's parameter set (Trace 2: a frequency base and
+// scale per layer).
 // With caller tables (the Sophgo MLIR-based LLM compilation paper, Listings 1-2: cos / sin
 // gathered by position_ids) c and s / sgn are the table entries of the token's position.
 // These kernels evaluate it in fp64 and round once to f16 (nearest even), so a rotated K
@@ -32,11 +34,12 @@ inline int rope_chunks(const RopeTable &tab)
     return tab.half ? tab.n_pairs >> 3 : (kHeadDim >> 3) - (tab.off >> 3);
 }
 
-// x[rows, h, 128] rotated in place; one thread per (row, 16-byte chunk of the rotated
-// region), looping over the heads so the trig is shared by all heads of a row.
+// x[rows, h, 128] rotated in place, rows = units x t; one thread per (row, 16-byte chunk
+// of the rotated region), looping over the heads so the trig is shared by all heads of a
+// row.
 __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict__ x,
                                                            const int32_t *__restrict__ positions,
-                                                           int64_t rows, int h, RopeTable tab)
+                                                           int64_t rows, int t, int h, RopeTable tab)
 {
     const int first_chunk = tab.off >> 3;
     const int nchunks = tab.half ? tab.n_pairs >> 3 : (kHeadDim >> 3) - first_chunk;
@@ -46,6 +49,7 @@ __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict_
     const int c = first_chunk + (int)(idx % nchunks);
     const int64_t r = idx / nchunks;
     const int pos = positions[r];
+    const int set = rope_set(tab, (int)(r / t));
     if (tab.half) {
         const int c2 = c + (tab.n_pairs >> 3);
         for (int hh = 0; hh < h; ++hh) {
@@ -53,14 +57,14 @@ __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict_
             Chunk16 a, b, ya, yb;
             a.v = p[c];
             b.v = p[c2];
-            rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab);
+            rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab, set);
             p[c] = ya.v;
             p[c2] = yb.v;
         }
         return;
     }
     double cs[4], sn[4];
-    chunk_trig(c, pos, tab, cs, sn);
+    chunk_trig(c, pos, tab, set, cs, sn);
     for (int hh = 0; hh < h; ++hh) {
         uint4 *p = reinterpret_cast<uint4 *>(x + (r * h + hh) * kHeadDim) + c;
         Chunk16 in, out;
@@ -128,6 +132,7 @@ __global__ void __launch_bounds__(256) rope_append_kernel(
         // writes both; a second-half chunk only copies V
         const int first_chunk = tab.off >> 3, h8 = tab.n_pairs >> 3;
         const int pos = positions[ti];
+        const int set = rope_set(tab, u);
         for (int g = 0; g < hkv; ++g) {
             const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
             const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
@@ -139,7 +144,7 @@ __global__ void __launch_bounds__(256) rope_append_kernel(
                 Chunk16 a, b, ya, yb;
                 a.v = ks[c];
                 b.v = ks[c + h8];
-                rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab);
+                rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab, set);
                 kd[c] = ya.v;
                 kd[c + h8] = yb.v;
             }
@@ -150,7 +155,7 @@ __global__ void __launch_bounds__(256) rope_append_kernel(
     double cs[4], sn[4];
     const bool rotated = 8 * c + 7 >= tab.off;
     if (rotated)
-        chunk_trig(c, positions[ti], tab, cs, sn);
+        chunk_trig(c, positions[ti], tab, rope_set(tab, u), cs, sn);
     for (int g = 0; g < hkv; ++g) {
         const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
         const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
@@ -169,14 +174,14 @@ inline unsigned grid_for(int64_t threads, int block) { return (unsigned)((thread
 
 } // namespace
 
-hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int h,
+hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t rows, int t, int h,
                                const RopeTable &tab, hipStream_t stream)
 {
     const int64_t threads = rows * rope_chunks(tab);
     if (threads == 0)
         return hipSuccess;
     hipLaunchKernelGGL(rope_inplace_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
-                       x, positions, rows, h, tab);
+                       x, positions, rows, t, h, tab);
     return hipGetLastError();
 }
 

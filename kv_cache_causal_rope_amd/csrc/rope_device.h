@@ -59,11 +59,14 @@ __device__ inline void sincos_turns(double r, double &s, double &c)
     }
 }
 
-// c and s of rotated pair j at position pos (NaN when a table does not cover pos)
-__device__ inline void pair_factor(int j, int pos, const RopeTable &tab, double &c, double &s)
+// c and s of rotated pair j at position pos under parameter set `set` (rope_set); NaN
+// when a table does not cover pos or the set index was invalid
+__device__ inline void pair_factor(int j, int pos, const RopeTable &tab, int set, double &c, double &s)
 {
 #pragma clang fp contract(off)
-    if (tab.cos_t) {
+    if (set < 0) {
+        c = s = __builtin_nan("");
+    } else if (tab.cos_t) {
         if (pos >= 0 && pos < tab.rows) {
             c = (double)tab.cos_t[(int64_t)pos * tab.n_pairs + j];
             s = (double)tab.sin_t[(int64_t)pos * tab.n_pairs + j] * tab.sgn;
@@ -72,14 +75,14 @@ __device__ inline void pair_factor(int j, int pos, const RopeTable &tab, double 
         }
     } else {
         double sv, cv;
-        sincos_turns((double)pos * tab.wrev[j], sv, cv);
-        c = cv * tab.mscale;
-        s = sv * tab.mscale * tab.sgn;
+        sincos_turns((double)pos * tab.wrev[set][j], sv, cv);
+        c = cv * tab.mscale[set];
+        s = sv * tab.mscale[set] * tab.sgn;
     }
 }
 
 // adjacent pairing: the factors of the four pairs of chunk c (identity before `off`)
-__device__ inline void chunk_trig(int c, int pos, const RopeTable &tab, double (&cs)[4],
+__device__ inline void chunk_trig(int c, int pos, const RopeTable &tab, int set, double (&cs)[4],
                                   double (&sn)[4])
 {
 #pragma unroll
@@ -88,20 +91,20 @@ __device__ inline void chunk_trig(int c, int pos, const RopeTable &tab, double (
         cs[m] = 1.0;
         sn[m] = 0.0;
         if (dim >= tab.off)
-            pair_factor((dim - tab.off) >> 1, pos, tab, cs[m], sn[m]);
+            pair_factor((dim - tab.off) >> 1, pos, tab, set, cs[m], sn[m]);
     }
 }
 
 // half-split pairing: chunk c0 of the first rotated half and its partner chunk
 // c0 + n_pairs / 8 hold the two dims of pairs 8 (c0 - off / 8) + e, e = 0 .. 7
 __device__ inline void rotate_half_chunks(const uint16_t (&a)[8], const uint16_t (&b)[8], uint16_t (&ya)[8],
-                                          uint16_t (&yb)[8], int j0, int pos, const RopeTable &tab)
+                                          uint16_t (&yb)[8], int j0, int pos, const RopeTable &tab, int set)
 {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         double c, s;
-        pair_factor(j0 + e, pos, tab, c, s);
+        pair_factor(j0 + e, pos, tab, set, c, s);
         const double x0 = h2d(a[e]);
         const double x1 = h2d(b[e]);
         ya[e] = f64_to_f16_rne_dev(x0 * c - x1 * s);

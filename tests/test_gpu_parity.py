@@ -354,18 +354,197 @@ def test_out_of_range_length_yields_nan_and_no_write(kv):
 
 
 def test_measurement_probes_run(kv):
-    """The ceiling probes bench.py reports: the stream probe reads a small cache without
+    """The ceiling probes bench.py reports: the stream and plain-read probes read without
     error, and the MFMA probe records a shader clock between 0.5 and 3 GHz."""
+    from kv_cache_causal_rope_amd import probes
     cfg = custom(3, 1, 12, 2, 300, seed=900)
     inp = W.make_inputs(cfg, lens=np.array([0, 150, 299], np.int32))
     d = to_dev(inp)
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
-    kv.probe_stream(d.cache_k, d.cache_v, d.lens, 299, 128, sink)
+    probes.stream_rows(d.cache_k, d.cache_v, d.lens, 299, 128, sink)
+    probes.read(d.cache_k, 64, sink)
     blocks = 8
     clk = torch.zeros(4 + 4 * blocks, dtype=torch.int64, device="cuda")
-    kv.probe_mfma(blocks, 256, clk)
+    probes.mfma(blocks, 256, clk)
     torch.cuda.synchronize()
     c = clk[4:].view(blocks, 4).cpu().double()
     assert bool((c[:, 1] > c[:, 0]).all()) and bool((c[:, 3] > c[:, 2]).all())
     mhz = float(((c[:, 3] - c[:, 2]) / (c[:, 1] - c[:, 0])).mean()) * 100.0
     assert 500.0 < mhz < 3000.0, mhz
+
+
+# ------------------------------------------------------------------ streams and threads
+def test_decode_on_a_side_stream(kv):
+    """Decode launched on a stream other than torch's current one, with the output and
+    workspace allocated by the binding: the result matches the oracle even when the
+    current stream is kept busy with fresh allocations meanwhile."""
+    lens = [3000, 1200, 4000]
+    cfg = W.Config("custom", "decode", 3, 1, 1, 12, 2, 128, W.PLAIN_128, 0, 0, 4100, 950, "")
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32))
+    rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    _, ref64, _ = oracle.decode(bits(inp.q)[:, 0], bits(inp.k)[:, 0], bits(inp.v)[:, 0],
+                                inp.positions.numpy()[:, 0], rk, rv, inp.lens.numpy(), cfg.scale,
+                                ora_rope(cfg.rope))
+    d = to_dev(inp)
+    caches = [(d.cache_k.clone(), d.cache_v.clone()) for _ in range(4)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())      # the copies above are on the current stream
+    outs = []
+    for ck, cv in caches:
+        outs.append(kv.decode(d.q, d.k, d.v, d.positions, ck, cv, d.lens, max(lens), kv.RopeParams.plain(),
+                              stream=side))
+        junk = torch.full((1 << 22,), 3.0, device="cuda")      # reuses freed blocks at once
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        P.check_attention(bits(o)[:, 0], ref64, "decode on a side stream")
+
+
+def test_profile_hook_is_per_thread(kv):
+    """A hook set on one thread is recorded by that thread's next call only: a call on
+    another thread neither records nor clears it, and that thread's own hook is its own.
+    The events are first recorded around a GPU sleep of ~50 ms; a re-record around a
+    decode kernel brings their interval down to well under a millisecond."""
+    import threading
+    cfg = W.Config("custom", "decode", 2, 1, 1, 12, 2, 128, W.PLAIN_128, 0, 0, 600, 960, "")
+    d = to_dev(W.make_inputs(cfg, lens=np.array([500, 300], np.int32)))
+    rp = kv.RopeParams.plain()
+
+    def events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evs[0].record()
+        torch.cuda._sleep(100_000_000)
+        evs[1].record()
+        return evs
+
+    mine, theirs = events(), events()
+    torch.cuda.synchronize()
+    assert mine[0].elapsed_time(mine[1]) > 10.0 and theirs[0].elapsed_time(theirs[1]) > 10.0
+    kv.set_profile_events(mine[0], mine[1])
+    errors = []
+
+    def other():
+        try:
+            torch.cuda.set_device(0)
+            kv.decode(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, 500, rp)   # no hook here
+            kv.set_profile_events(theirs[0], theirs[1])
+            kv.decode(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, 500, rp)
+            torch.cuda.synchronize()
+        except Exception as e:  # noqa: BLE001
+            errors.append(e)
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    assert mine[0].elapsed_time(mine[1]) > 10.0          # untouched by the other thread
+    assert theirs[0].elapsed_time(theirs[1]) < 1.0       # recorded by its own call there
+    kv.decode(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, 500, rp)
+    torch.cuda.synchronize()
+    assert mine[0].elapsed_time(mine[1]) < 1.0           # recorded by this thread's call
+
+
+# ------------------------------------------------------------------ per-unit parameter sets
+def _set_batch():
+    """Layers of two kinds in one batch (ds4.c study notes, Part 4 sec. 1, Trace 2): plain
+    RoPE with base 1e4, and "compressed" layers with their own base and scale and the YaRN
+    ramp on (the rotated width is shared by all sets: the whole head here)."""
+    plain = W.PLAIN_128
+    compressed = W.Rope(base=160000.0, n_rot=128, yarn=True, freq_scale=1.0 / 16, ext_factor=1.0,
+                        n_ctx_orig=65536, beta_fast=32.0, beta_slow=1.0, mscale=1.0 + 0.1 * np.log(16.0))
+    return [plain, compressed]
+
+
+def _kv_sets(kv, sets, unit_set):
+    rp = kv.RopeParams.from_fields(sets[0])
+    return rp.with_sets([kv.RopeParams.from_fields(s) for s in sets],
+                        torch.tensor(unit_set, dtype=torch.int32, device="cuda"))
+
+
+@pytest.mark.parametrize("lens", [[0, 0, 0, 0, 0], [37, 0, 300, 64, 5]])
+def test_parameter_sets_prefill_kv(kv, lens):
+    sets, unit_set = _set_batch(), [1, 0, 1, 1, 0]
+    n, t, hq, hkv = 5, 70, 12, 2
+    cfg = custom(n, t, hq, hkv, max(lens) + t + 3, seed=970)
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32))
+    rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    ref = oracle.prefill_kv(bits(inp.q), bits(inp.k), bits(inp.v), inp.positions.numpy(), rk, rv,
+                            inp.lens.numpy(), cfg.scale, [ora_rope(s) for s in sets], np.array(unit_set))
+    d = to_dev(inp)
+    rp = _kv_sets(kv, sets, unit_set)
+    if max(lens) == 0:
+        out = kv.prefill(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, rp, scale=cfg.scale)
+    else:
+        out = kv.prefill_kv(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, max(lens), rp,
+                            scale=cfg.scale)
+    torch.cuda.synchronize()
+    check_prefill(d, out, (ref[0], ref[1], ref[2], rk, rv), lens, t, f"parameter sets {lens}")
+
+
+def test_parameter_sets_decode_and_rope_apply(kv):
+    sets, unit_set = _set_batch(), [0, 1, 1, 0]
+    lens = [900, 20000, 4097, 3]
+    d, out, ref = None, None, None
+    cfg = W.Config("custom", "decode", 4, 1, 1, 32, 8, 128, W.PLAIN_128, 0, 0, 20005, 980, "")
+    inp = W.make_inputs(cfg, lens=np.asarray(lens, np.int32))
+    rk, rv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
+    ora_sets = [ora_rope(s) for s in sets]
+    ref = oracle.decode(bits(inp.q)[:, 0], bits(inp.k)[:, 0], bits(inp.v)[:, 0], inp.positions.numpy()[:, 0],
+                        rk, rv, inp.lens.numpy(), cfg.scale, ora_sets, np.array(unit_set))
+    d = to_dev(inp)
+    rp = _kv_sets(kv, sets, unit_set)
+    out = kv.decode(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, d.lens, max(lens), rp, scale=cfg.scale)
+    torch.cuda.synchronize()
+    check_decode(d, out, (ref[0], ref[1], ref[2], rk, rv), lens, "decode with parameter sets")
+    # rope_apply: unit u of x [n, t, h, 128] rotates with its set
+    g = torch.Generator().manual_seed(981)
+    x = torch.randn((4, 9, 3, 128), generator=g).half()
+    pos = torch.randint(0, 30000, (4, 9), generator=g, dtype=torch.int32)
+    ref_bits = np.empty(bits(x).shape, np.uint16)
+    ref64 = np.empty(ref_bits.shape)
+    for u in range(4):
+        ref_bits[u], ref64[u] = oracle.rope(bits(x)[u], pos.numpy()[u], ora_sets[unit_set[u]])
+    xd = x.cuda()
+    kv.rope_apply(xd, pos.cuda(), rp)
+    torch.cuda.synchronize()
+    P.check_k_rows(bits(xd), ref_bits, ref64, "rope_apply with parameter sets")
+
+
+def test_invalid_parameter_set_index_gives_nan_rotation(kv):
+    sets = _set_batch()
+    cfg = custom(2, 8, 12, 2, 8, seed=985)
+    d = to_dev(W.make_inputs(cfg, lens=np.zeros(2, np.int32)))
+    rp = _kv_sets(kv, sets, [1, 7])
+    out = kv.prefill(d.q, d.k, d.v, d.positions, d.cache_k, d.cache_v, rp, scale=cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[0]).all() and torch.isnan(out[1]).all()
+    assert torch.isnan(d.cache_k[1]).all() and torch.isfinite(d.cache_v[1]).all()
+
+
+# ------------------------------------------------------------------ phase consistency, long positions
+def test_gpu_prefill_kv_equals_successive_gpu_decodes_near_32k(kv):
+    """The K rows the prefill side writes (rope_append) and those the decode prologue
+    writes agree bit for bit at positions just below 32k, where the angle reduction is
+    hardest (plain and YaRN tail rotation)."""
+    for rope in (W.PLAIN_128, W.YARN_TAIL_64):
+        n, t, hq, hkv, hist = 2, 24, 32, 8, 32700
+        cfg = custom(n, t, hq, hkv, hist + t, rope=rope, seed=990)
+        inp = W.make_inputs(cfg, lens=np.full(n, hist, np.int32))
+        d = to_dev(inp)
+        rp = kv.RopeParams.from_fields(rope)
+        ck1, cv1 = d.cache_k.clone(), d.cache_v.clone()
+        out1 = kv.prefill_kv(d.q, d.k, d.v, d.positions, ck1, cv1, d.lens, hist, rp)
+        ck2, cv2 = d.cache_k.clone(), d.cache_v.clone()
+        outs = []
+        for i in range(t):
+            lens = torch.full((n,), hist + i, dtype=torch.int32, device="cuda")
+            outs.append(kv.decode(d.q[:, i:i + 1].contiguous(), d.k[:, i:i + 1].contiguous(),
+                                  d.v[:, i:i + 1].contiguous(), d.positions[:, i].contiguous(),
+                                  ck2, cv2, lens, hist + i, rp))
+        torch.cuda.synchronize()
+        assert torch.equal(ck1.view(torch.int16), ck2.view(torch.int16)), rope
+        assert torch.equal(cv1.view(torch.int16), cv2.view(torch.int16))
+        diff = (out1.double() - torch.cat(outs, dim=1).double()).abs().max().item()
+        assert diff <= 2e-3, diff
