@@ -192,6 +192,26 @@ int attn_decode(const void *q, const void *k, const void *v, const int32_t *posi
                 const kvrope_rope_params *rp, void *workspace, size_t ws_bytes,
                 void *stream);
 
+/* attn_decode_noalloc -- attn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same steps, kernels and results, with the split-key partials kept in a scratch
+ * array the library holds on each GPU (attn_decode_noalloc_max_workspace() bytes, 64 MiB,
+ * for the life of the process) instead of a caller workspace.  The call allocates and
+ * frees nothing.  Shapes whose workspace (attn_workspace_size(ATTN_OP_DECODE, ...))
+ * exceeds the scratch size return ATTN_ERR_WORKSPACE before any HIP call; the first call
+ * on a device looks up that device's scratch address (hipGetSymbolAddress; a failure is
+ * ATTN_ERR_HIP).  Every call on one GPU shares its scratch: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race and may
+ * return wrong outputs; calls ordered on one stream are safe.  No part of the scratch
+ * needs to start at zero.  Everything else as attn_decode. */
+int attn_decode_noalloc(const void *q, const void *k, const void *v, const int32_t *positions,
+                        void *cache_k, void *cache_v, const int32_t *cache_lens, int max_len,
+                        void *out, int n, int hq, int hkv, int d, int s_cap, double scale,
+                        const kvrope_rope_params *rp, void *stream);
+
+/* Bytes of device scratch attn_decode_noalloc holds per GPU (its workspace limit). */
+size_t attn_decode_noalloc_max_workspace(void);
+
 /* ---- The projections either side of attention ([Sophgo] Listings 1-2: q, k, v =
  * MatMul(x, w_q / w_k / w_v), Rope on q and k, Concat into the cache; h = Add(input,
  * MatMul(attn, w_o))), on f16 MFMA with fp32 accumulation.  Weights are stored one row per

@@ -40,7 +40,7 @@ MAX_ROPE_SETS = 4
 EXPORTS = ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
            "attn_prefill_kv_varlen", "attn_decode", "attn_workspace_size", "attn_status_string",
            "attn_last_hip_error", "attn_set_profile_events", "attn_qkv_project", "attn_out_project",
-           "attn_prefill_kv_cached"]
+           "attn_prefill_kv_cached", "attn_decode_noalloc", "attn_decode_noalloc_max_workspace"]
 
 
 class KVRopeError(RuntimeError):
@@ -167,6 +167,9 @@ def lib() -> ctypes.CDLL:
                                          [ctypes.c_double, rp, _P])
     L.attn_decode.argtypes = ([_P] * 7 + [_I, _P] + [_I] * 5 +
                               [ctypes.c_double, rp, _P, ctypes.c_size_t, _P])
+    L.attn_decode_noalloc.argtypes = ([_P] * 7 + [_I, _P] + [_I] * 5 + [ctypes.c_double, rp, _P])
+    L.attn_decode_noalloc_max_workspace.argtypes = []
+    L.attn_decode_noalloc_max_workspace.restype = ctypes.c_size_t
     L.attn_workspace_size.argtypes = [_I] * 7
     L.attn_workspace_size.restype = ctypes.c_size_t
     L.attn_status_string.argtypes = [_I]
@@ -178,7 +181,7 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_kv_cached.argtypes = [_P] * 5 + [_I, _P] + [_I] * 6 + [ctypes.c_double, rp, _P]
     for rtn in ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
                 "attn_prefill_kv_varlen", "attn_decode", "attn_set_profile_events", "attn_qkv_project",
-                "attn_out_project", "attn_prefill_kv_cached"]:
+                "attn_out_project", "attn_prefill_kv_cached", "attn_decode_noalloc"]:
         getattr(L, rtn).restype = _I
     _lib = L
     return L

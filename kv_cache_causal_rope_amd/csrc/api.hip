@@ -9,7 +9,50 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace {
+
+// Device scratch of attn_decode_noalloc: the split-key partials, in a file-scope array
+// every GPU the library runs on holds until the process ends.  Host code never uses the
+// array's name as an address: it takes each device's own address once, through
+// hipGetSymbolAddress, and passes that to the kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The scratch address on the current device (set up on the first call there), or NULL
+// with *err set.
+void *device_scratch(hipError_t *err)
+{
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !p) {
+            if (*err == hipSuccess)
+                *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 // the library's only state, per thread
 thread_local int g_last_hip_error = 0;
@@ -359,6 +402,28 @@ int attn_decode(const void *q, const void *k, const void *v, const int32_t *posi
                                             cache_lens, static_cast<uint16_t *>(out), ds, tab, workspace,
                                             static_cast<hipStream_t>(stream), eb, ea));
 }
+
+int attn_decode_noalloc(const void *q, const void *k, const void *v, const int32_t *positions,
+                        void *cache_k, void *cache_v, const int32_t *cache_lens, int max_len,
+                        void *out, int n, int hq, int hkv, int d, int s_cap, double scale,
+                        const kvrope_rope_params *rp, void *stream)
+{
+    // the size check needs valid shapes; every other check is attn_decode's
+    if (n >= 0 && hq >= 1 && hkv >= 1 && hq % hkv == 0 && max_len >= 0 &&
+        kvrope::decode_workspace_bytes(n, hq, hkv, max_len) > kScratchBytes)
+        return ATTN_ERR_WORKSPACE;
+    hipError_t e = hipSuccess;
+    void *ws = nullptr;
+    if (n > 0 && hq >= 1 && hkv >= 1 && hq % hkv == 0 && max_len >= 0) {
+        ws = device_scratch(&e);
+        if (!ws)
+            return hip_status(e);
+    }
+    return attn_decode(q, k, v, positions, cache_k, cache_v, cache_lens, max_len, out, n, hq, hkv, d, s_cap,
+                       scale, rp, ws, ws ? kScratchBytes : 0, stream);
+}
+
+size_t attn_decode_noalloc_max_workspace(void) { return kScratchBytes; }
 
 int attn_prefill_kv_cached(const void *q, const int32_t *positions, const void *cache_k, const void *cache_v,
                            const int32_t *hist_lens, int max_hist, void *out, int n, int t, int hq, int hkv,
