@@ -51,18 +51,8 @@ TRAFFIC = {
         "src": ("12abee6e1d6421ceaeab530940b87c00a6bbe19002417370de3ce5de3b625815",
                 "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
                 "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
-    "decode_split:qwen1p5b_decode_l4096_b32": {
-        "bytes": 2.83175e9,
-        "src": ("539ae65605d09c5c2f1885ac90290ee409e898a4480e07279581126dde283480",
-                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
-                "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
-    "decode_split:yarn_decode_l32k_b64": {
-        "bytes": 23.03663e9,
-        "src": ("539ae65605d09c5c2f1885ac90290ee409e898a4480e07279581126dde283480",
-                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
-                "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
 }
-KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_split": "decode.hip"}
+KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_attn": "decode.hip"}
 
 
 def log(*a):
@@ -163,34 +153,70 @@ def bench_decode(kv, W, name, steps, warmup):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    # whole step (rotation + append + attention kernel, then the combine kernel): events
+    # around the call only
     ca, cb = make_events(steps), make_events(steps)
-    evb, eva = make_events(steps), make_events(steps)
     for i in range(steps):
         flush.sum()                    # evict the Infinity Cache between steps
         ca[i].record()
-        kv.set_profile_events(evb[i], eva[i])
         call()
         cb[i].record()
     torch.cuda.synchronize()
     call_ms = sum(ca[i].elapsed_time(cb[i]) for i in range(steps)) / steps
+    # the attention kernel alone, in a pass of its own: the library's events around it
+    evb, eva = make_events(steps), make_events(steps)
+    for i in range(steps):
+        flush.sum()
+        kv.set_profile_events(evb[i], eva[i])
+        call()
+    torch.cuda.synchronize()
     k_ms = sum(evb[i].elapsed_time(eva[i]) for i in range(steps)) / steps
     nbytes = decode_bytes(lens, cfg.hq, cfg.hkv, cfg.d)
+    # the attention kernel moves all of it except the output rows, which the combine
+    # kernel writes
+    kbytes = nbytes - cfg.n * cfg.hq * cfg.d * 2
     # measured ceiling of this access pattern: a kernel that only reads the same cache
-    # rows (rows 0..len of K and V, 1536-row chunks per workgroup, as the split kernel
-    # takes for these shapes), timed the same way
+    # rows (rows 0..len of K and V), split into chunks exactly as the decode kernel splits
+    # them for this shape, timed the same way
+    chunk = kv.decode_chunk_keys(cfg.n, cfg.hq, cfg.hkv, max_len)
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
     pa, pb = make_events(steps), make_events(steps)
     for i in range(steps):
         flush.sum()
         pa[i].record()
-        probes.stream_rows(inp.cache_k, inp.cache_v, inp.lens, max_len, 1536, sink)
+        probes.stream_rows(inp.cache_k, inp.cache_v, inp.lens, max_len, chunk, sink)
         pb[i].record()
     torch.cuda.synchronize()
     probe_ms = sum(pa[i].elapsed_time(pb[i]) for i in range(steps)) / steps
     probe_bytes = 2 * cfg.hkv * cfg.d * 2 * int((lens.astype(np.int64) + 1).sum())
     del inp, flush, ws
     torch.cuda.empty_cache()
-    return cfg, call_ms, k_ms, nbytes, probe_bytes / probe_ms / 1e6
+    return cfg, call_ms, k_ms, nbytes, kbytes, probe_bytes / probe_ms / 1e6, chunk
+
+
+def measured_hbm_read():
+    """The plain HBM read ceiling: a 4 GiB buffer read once front to back with 16-byte lane
+    loads (Infinity Cache evicted first), best of a few grid sizes and repeats."""
+    import torch
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(128 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    best = (0.0, 0)
+    for blocks in (256, 1024, 4096, 8192):
+        for _ in range(3):
+            flush.sum()
+            e0, e1 = make_events(2)
+            e0.record()
+            probes.read(buf, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            best = max(best, (gbs, blocks))
+    del buf, flush
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbs": round(best[0], 1),
+            "what": f"4 GiB read once with 16-byte lane loads, best of 4 grid sizes x 3 runs "
+                    f"({best[1]} workgroups); Infinity Cache evicted before each run"}
 
 
 def measured_mfma(kv):
@@ -260,27 +286,64 @@ def bench_projections(kv, steps, warmup):
     return res
 
 
-def cpu_baseline(W, name, units):
-    """The oracle (untuned, fp64, OpenMP) on `units` layers of the prefill workload."""
+def oracle_time(W, name, units, threads):
+    """Seconds the oracle (untuned, fp64, OpenMP on `threads` threads) takes for `units`
+    layers of a prefill workload, run in this process (which touches no GPU); prints one
+    JSON line."""
     import numpy as np
+    import torch
     import oracle
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg, n=units)
-    bits = lambda x: x.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    bits = lambda x: x.contiguous().view(torch.int16).numpy().view(np.uint16)
     ck, cv = bits(inp.cache_k).copy(), bits(inp.cache_v).copy()
     r = cfg.rope
     rp = oracle.RopeParams(base=r.base, n_rot=r.n_rot, yarn=r.yarn, freq_scale=r.freq_scale,
                            ext_factor=r.ext_factor, n_ctx_orig=r.n_ctx_orig, beta_fast=r.beta_fast,
                            beta_slow=r.beta_slow, mscale=r.mscale)
+    oracle.set_num_threads(threads)
     t0 = time.perf_counter()
     oracle.prefill_kv(bits(inp.q), bits(inp.k), bits(inp.v), inp.positions.numpy(), ck, cv,
                       inp.lens.numpy(), cfg.scale, rp)
     sec = time.perf_counter() - t0
     flops = prefill_flops(units, cfg.t, cfg.hq, cfg.d, inp.lens.numpy())
-    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    print(json.dumps({"sec": sec, "flops": flops, "threads": oracle.num_threads()}), flush=True)
+
+
+def cpu_baseline(name, st_units):
+    """The oracle on the whole prefill workload with every host thread, and single-threaded
+    on the tiny T = 64 workload and on `st_units` layers of the prefill workload; each run
+    in a child process that touches no GPU."""
+    import subprocess
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+
+    def run(workload, units, nthreads):
+        out = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-time", workload, str(units),
+                              str(nthreads)], capture_output=True, text=True, check=True).stdout
+        return json.loads(out.strip().splitlines()[-1])
+
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    full = run(name, 28, threads)
+    tiny = run("tiny_prefill_t64", 1, 1)
+    one = run(name, st_units, 1)
+    return {"value": full["flops"] / full["sec"] / 1e12, "unit": "TFLOP/s", "cores": full["threads"],
             "kind": "oracle",
-            "sample": f"{units} of {cfg.n} layers of {name} (T={cfg.t}, {cfg.hq}q/{cfg.hkv}kv x "
-                      f"{cfg.d}), full causal prefill incl. rotary + append, {sec:.1f} s"}
+            "sample": f"all 28 layers of {name} (T=1024, 12q/2kv x 128), full causal prefill incl. "
+                      f"rotary + append, {full['sec']:.1f} s on {full['threads']} threads",
+            "cpu_model": model,
+            "single_thread": {
+                "threads": one["threads"],
+                "tiny_prefill_t64_s": round(tiny["sec"], 4),
+                "tiny_prefill_t64_tflops": tiny["flops"] / tiny["sec"] / 1e12,
+                f"{name}_{st_units}_layers_s": round(one["sec"], 2),
+                f"{name}_tflops": one["flops"] / one["sec"] / 1e12}}
 
 
 def main():
@@ -289,7 +352,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen1p5b_prefill_t1024")
-    ap.add_argument("--cpu-units", type=int, default=8)
+    ap.add_argument("--cpu-single-thread-units", type=int, default=4,
+                    help="layers of the prefill workload the single-thread oracle run takes")
+    ap.add_argument("--oracle-time", nargs=3, metavar=("WORKLOAD", "UNITS", "THREADS"),
+                    help=argparse.SUPPRESS)  # child process of the CPU baseline
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-projections", action="store_true")
@@ -299,6 +365,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.oracle_time:
+        from kv_cache_causal_rope_amd import workloads as W
+        oracle_time(W, args.oracle_time[0], int(args.oracle_time[1]), int(args.oracle_time[2]))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this attention path runs on a single MI355X "
               "(no collectives); rerun with --gpus 1", file=sys.stderr)
@@ -355,10 +425,10 @@ def main():
             names += ["qwen1p5b_decode_l1024_b1", "qwen1p5b_decode_l4096_b1"]
         for name in names:
             log(f"[bench] decode {name}")
-            dcfg, call_ms, dk_ms, nbytes, ceil_gbs = bench_decode(kv, W, name, max(3, args.steps // 2),
-                                                                  min(args.warmup, 3))
+            dcfg, call_ms, dk_ms, nbytes, kbytes, ceil_gbs, chunk = bench_decode(
+                kv, W, name, max(3, args.steps // 2), min(args.warmup, 3))
             gbs = nbytes / (call_ms * 1e-3) / 1e9
-            kgbs = nbytes / (dk_ms * 1e-3) / 1e9
+            kgbs = kbytes / (dk_ms * 1e-3) / 1e9
             log(f"[bench] decode {name}: {call_ms * 1e3:.1f} us/step, split kernel "
                 f"{dk_ms * 1e3:.1f} us, {gbs:.0f} GB/s step, {kgbs:.0f} GB/s kernel; "
                 f"read-only stream of the same rows {ceil_gbs:.0f} GB/s")
@@ -368,10 +438,13 @@ def main():
                            "roofline": {"bound": "hbm", "achieved": round(kgbs, 1),
                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                         "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                                        "traffic": traffic("decode_split", name)},
+                                        "traffic": traffic("decode_attn", name),
+                                        "kernel_bytes": kbytes,
+                                        "what": "attention kernel (rotation, append, split-key "
+                                                "attention); its bytes exclude the output rows"},
                            "stream_ceiling": {"value": round(ceil_gbs, 1), "unit": "GB/s",
-                                              "what": "read-only kernel over the same cache rows, "
-                                                      "same chunking",
+                                              "what": f"read-only kernel over the same cache rows, "
+                                                      f"same split ({chunk}-key chunks at most)",
                                               "kernel_frac": round(kgbs / ceil_gbs, 4)}})
 
     proj = None
@@ -382,14 +455,17 @@ def main():
             f"({proj['out_project']['us']:.1f} us)")
 
     ceilings = measured_mfma(kv)
+    ceilings.update(measured_hbm_read())
+    log(f"[bench] plain HBM read: {ceilings['hbm_read_gbs']:.0f} GB/s")
     log(f"[bench] f16 MFMA microbenchmark: {ceilings['mfma_f16_tflops']:.0f} TFLOP/s at "
         f"{ceilings['sclk_mhz']:.0f} MHz shader clock")
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_units} layers")
-        cpu = cpu_baseline(W, args.workload, args.cpu_units)
-        log(f"[bench] cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+        log(f"[bench] cpu baseline: oracle on all 28 layers, then single-threaded runs")
+        cpu = cpu_baseline(args.workload, args.cpu_single_thread_units)
+        log(f"[bench] cpu baseline: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads "
+            f"({cpu['cpu_model']}); single thread {cpu['single_thread']}")
 
     line = {
         "metric": METRIC,

@@ -259,6 +259,12 @@ int attn_out_project(const void *attn, const void *w_o, int w_per_unit, const vo
 /* Bytes of device workspace the operation needs (0 for operations that need none). */
 size_t attn_workspace_size(int op, int n, int t, int hq, int hkv, int d, int max_len);
 
+/* How attn_decode splits the work for this shape: a unit's cache_lens[u] + 1 keys are cut
+ * into the fewest chunks of at most this many keys (a multiple of 32), of equal size
+ * rounded up to 32 keys, one workgroup per chunk (0 for an invalid shape).  For
+ * benchmarks that reproduce the same access pattern. */
+int attn_decode_chunk_keys(int n, int hq, int hkv, int max_len);
+
 /* Static description of a status code (never NULL). */
 const char *attn_status_string(int status);
 

@@ -28,8 +28,9 @@ int kvprobe_read(const void *buf, size_t bytes, int blocks, void *sink, void *st
 
 /* kvprobe_stream -- reads, and only reads, the cache rows a decode step reads: rows
  * [0, lens[u]] of K and V of every (unit, KV head) (caches [n, hkv, s_cap, d], lens
- * device int32 [n]), split into chunks of `chunk` rows (a multiple of 32) per workgroup,
- * 16-byte lane loads.  Its time is the streaming ceiling of that access pattern.
+ * device int32 [n]), one workgroup per chunk, a unit's rows cut as attn_decode cuts them
+ * for chunk = attn_decode_chunk_keys(...) (the fewest chunks of at most `chunk` rows, of
+ * equal size rounded up to 32), 16-byte lane loads.  Its time is the streaming ceiling of that access pattern.
  * Requires max_len + 1 <= s_cap (every lens[u] <= max_len); a row past s_cap is never
  * read.  sink: >= 4 bytes. */
 int kvprobe_stream(const void *cache_k, const void *cache_v, const int32_t *lens, int n, int hkv,

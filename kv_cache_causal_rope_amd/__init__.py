@@ -40,7 +40,8 @@ MAX_ROPE_SETS = 4
 EXPORTS = ["attn_rope_apply", "kv_cache_append", "attn_prefill", "attn_prefill_kv",
            "attn_prefill_kv_varlen", "attn_decode", "attn_workspace_size", "attn_status_string",
            "attn_last_hip_error", "attn_set_profile_events", "attn_qkv_project", "attn_out_project",
-           "attn_prefill_kv_cached", "attn_decode_noalloc", "attn_decode_noalloc_max_workspace"]
+           "attn_prefill_kv_cached", "attn_decode_noalloc", "attn_decode_noalloc_max_workspace",
+           "attn_decode_chunk_keys"]
 
 
 class KVRopeError(RuntimeError):
@@ -170,6 +171,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_noalloc.argtypes = ([_P] * 7 + [_I, _P] + [_I] * 5 + [ctypes.c_double, rp, _P])
     L.attn_decode_noalloc_max_workspace.argtypes = []
     L.attn_decode_noalloc_max_workspace.restype = ctypes.c_size_t
+    L.attn_decode_chunk_keys.argtypes = [_I] * 4
+    L.attn_decode_chunk_keys.restype = _I
     L.attn_workspace_size.argtypes = [_I] * 7
     L.attn_workspace_size.restype = ctypes.c_size_t
     L.attn_status_string.argtypes = [_I]
@@ -235,6 +238,11 @@ def _alloc(stream, make):
         return make()
     with torch.cuda.stream(stream):
         return make()
+
+
+def decode_chunk_keys(n: int, hq: int, hkv: int, max_len: int) -> int:
+    """Keys per chunk (at most) attn_decode splits a unit's keys into for this shape."""
+    return int(lib().attn_decode_chunk_keys(n, hq, hkv, max_len))
 
 
 def workspace_size(n: int, hq: int, hkv: int, max_len: int, d: int = 128) -> int:

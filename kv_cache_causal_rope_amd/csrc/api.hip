@@ -245,6 +245,13 @@ size_t attn_workspace_size(int op, int n, int t, int hq, int hkv, int d, int max
     return kvrope::decode_workspace_bytes(n, hq, hkv, max_len);
 }
 
+int attn_decode_chunk_keys(int n, int hq, int hkv, int max_len)
+{
+    if (n <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_len < 0)
+        return 0;
+    return kvrope::decode_chunk_keys(n, hq, hkv, max_len);
+}
+
 int attn_rope_apply(void *x, const int32_t *positions, int n, int t, int h, int d,
                     const kvrope_rope_params *rp, void *stream)
 {

@@ -56,6 +56,8 @@ struct DecodeShape {
 
 // Bytes of fp32 workspace the split-key decode needs for this shape.
 size_t decode_workspace_bytes(int n, int hq, int hkv, int max_len);
+// Keys per chunk (at most) the split-key decode cuts a unit's keys into for this shape.
+int decode_chunk_keys(int n, int hq, int hkv, int max_len);
 
 hipError_t launch_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          const int32_t *positions, uint16_t *cache_k, uint16_t *cache_v,

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(256) read_kernel(const u32x4 *__restrict__ buf
         sink[0] = acc;
 }
 
-// One workgroup per (unit, KV head, chunk of `chunk` rows), 256 threads; rows
+// One workgroup per (unit, KV head, chunk), 256 threads; rows
 // [0, lens[u]] of K and V (the cache rows of a decode step with the new row appended).
 // Each iteration reads 16 rows of K and 16 of V (4 KB each) as 16-byte lane loads, four
 // iterations in flight.
@@ -58,10 +58,14 @@ __global__ void __launch_bounds__(256) stream_rows_kernel(const uint16_t *__rest
     b /= nsplit;
     const int g = b % hkv, u = b / hkv;
     const int nk = lens[u] + 1;
-    const int k0 = split * chunk;
+    // the unit's keys in the fewest chunks of at most `chunk` keys, of equal size rounded
+    // up to 32 (the decode kernel's split)
+    const int want = (nk + chunk - 1) / chunk;
+    const int cu = ((nk + want - 1) / want + 31) / 32 * 32;
+    const int k0 = split * cu;
     if (k0 >= nk)
         return;
-    const int k1 = min(min(k0 + chunk, nk), s_cap);
+    const int k1 = min(min(k0 + cu, nk), s_cap);
     const size_t slab = ((size_t)u * hkv + g) * (size_t)s_cap * kHeadDim;
     const u32x4 *K = reinterpret_cast<const u32x4 *>(ck + slab);
     const u32x4 *V = reinterpret_cast<const u32x4 *>(cv + slab);

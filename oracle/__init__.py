@@ -144,6 +144,7 @@ def load(path: str) -> ctypes.CDLL:
     L.ora_decode.argtypes = ([_P] * 8 + [ctypes.c_int] * 5 +
                              [ctypes.c_double, _P, _P, _P, _P])
     L.ora_num_threads.restype = ctypes.c_int
+    L.ora_set_num_threads.argtypes = [ctypes.c_int]
     return L
 
 
@@ -187,6 +188,11 @@ def _i32(a) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().ora_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use (for timing runs; results do not depend on it)."""
+    lib().ora_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- f16 codec

@@ -531,3 +531,14 @@ int ora_num_threads(void)
     return 1;
 #endif
 }
+
+/* threads the parallel loops use from now on (timing runs only; no effect on results) */
+void ora_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
