@@ -47,10 +47,35 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 267.407e6,
-        "src": ("12abee6e1d6421ceaeab530940b87c00a6bbe19002417370de3ce5de3b625815",
-                "76793c737a660be05557ba3d71cc67c8c2f52e27869ee58c39479923e8b2a53f",
-                "148804b2e769350326d9613b6ebf82f3bfda63683064f651456cbad6777b5773")},
+        "bytes": 2.6734e+08,
+        "src": ("e1740d62b86d7a50b16f5e21189e638be298326b5de5ca8e96eaadc9d4521b36",
+                "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
+                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+    "prefill_attn:h4096_prefill_kv_3840p256": {
+        "bytes": 6.5901e+08,
+        "src": ("e1740d62b86d7a50b16f5e21189e638be298326b5de5ca8e96eaadc9d4521b36",
+                "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
+                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+    "decode_attn:qwen1p5b_decode_l4096_b32": {
+        "bytes": 2.8411e+09,
+        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+                "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
+                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+    "decode_attn:yarn_decode_l32k_b64": {
+        "bytes": 2.3069e+10,
+        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+                "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
+                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+    "decode_attn:qwen1p5b_decode_l1024_b1": {
+        "bytes": 3.0548e+07,
+        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+                "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
+                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+    "decode_attn:qwen1p5b_decode_l4096_b1": {
+        "bytes": 7.2232e+07,
+        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+                "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
+                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
 }
 KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_attn": "decode.hip"}
 
