@@ -107,6 +107,7 @@ struct PrefillParams {
     int wpk;     // work units per (unit, KV head) = ceil(items / 8)
     int units;   // work units in all: n * hkv * wpk
     int xcd;     // grid size is a multiple of 8 (XCD-preserving snake order)
+    int pairmajor; // XCD-local, pair-major unit order (KV pairs a multiple of 8; see the kernel)
     float scale_log2;
 };
 
@@ -499,6 +500,10 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     // consecutive rounds evens out.  With P a multiple of 8 the reversal keeps w' = w
     // (mod 8): workgroups are dealt to the 8 XCDs round-robin, so when KP is a multiple
     // of 8 too, every unit of a pair runs on the same XCD and its K/V stays in that L2.
+    // Pair-major order (when the history dominates, so that the units of a pair cost about
+    // the same): XCD x takes the pairs x, x + 8, ... one after another, all units of a pair
+    // in the same round, heaviest rank first; so the XCD's workgroups stream one pair's K/V
+    // together instead of every pair's at once, and a tile leaves HBM about once.
     const int P = gridDim.x;
 
     // rotation tables of every parameter set, shared by every unit
@@ -522,11 +527,22 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         int slot = blockIdx.x;
         if (round & 1)
             slot = p.xcd ? ((P >> 3) - 1 - (slot >> 3)) * 8 + (slot & 7) : P - 1 - slot;
-        const int v = round * P + slot;
-        if (v >= p.units)
-            break;
-        const int rank = v / KP;
-        const int kp = v - rank * KP;
+        int v, rank, kp;
+        if (p.pairmajor) {
+            const int i = round * (P >> 3) + (slot >> 3); // unit index on this XCD
+            if (i >= (KP >> 3) * p.wpk)
+                break;
+            const int pl = i / p.wpk;
+            rank = i - pl * p.wpk;
+            kp = (slot & 7) + 8 * pl;
+            v = rank * KP + kp;
+        } else {
+            v = round * P + slot;
+            if (v >= p.units)
+                break;
+            rank = v / KP;
+            kp = v - rank * KP;
+        }
         const int wk = p.wpk - 1 - rank;
         const int u = kp / p.hkv, g = kp - u * p.hkv;
         const int item = wk * NW + wave;
@@ -994,6 +1010,10 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
         return e;
     const int64_t blocks = std::min<int64_t>(units, std::max(ncu, 1));
     p.xcd = (blocks % 8 == 0) ? 1 : 0;
+    // pair-major order when the history bounds the work per unit (the units of a pair then
+    // differ by at most t keys of their max_hist + t): measured 2-3 % faster on a 32-layer
+    // 3840 + 256 prefill_kv, 1-2 % slower on a T = 1024 prefill
+    p.pairmajor = (p.xcd && (s.n * s.hkv) % 8 == 0 && s.max_hist >= s.t) ? 1 : 0;
 
     if (ev_before)
         (void)hipEventRecord(ev_before, stream);

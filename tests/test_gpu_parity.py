@@ -146,6 +146,8 @@ def test_prefill_shapes(kv, n, t, hq, hkv):
     (3, 64, 12, 2, [0, 64, 130], W.PLAIN_128),
     (2, 29, 32, 8, [300, 5], W.YARN_TAIL_64),
     (1, 96, 6, 6, [1000], W.PLAIN_128),
+    # history >= t and 32 KV pairs: the pair-major unit order, over two rounds of the grid
+    (16, 200, 32, 2, [250 + 13 * u for u in range(16)], W.PLAIN_128),
 ])
 def test_prefill_kv_shapes(kv, n, t, hq, hkv, lens, rope):
     cfg = custom(n, t, hq, hkv, max(lens) + t + 5, rope=rope, seed=300 + t)
