@@ -21,11 +21,13 @@
 // product (the key order inside each 16-key step is permuted consistently on both
 // operands, which the reduction allows).
 //
-// Softmax: fp32, log2 domain (q carries scale * log2(e)).  The score accumulators start
-// at -m (m = the row's reference max), so S^T leaves the matrix core as (score - m).  m
-// is set exactly from a row's first tile and is otherwise left alone: the probabilities
-// 2^(score - m) are rounded to f16 for the PV product, so they may grow up to the f16
-// range (relative precision is the same at any magnitude) before anything must move.
+// Softmax: fp32, log2 domain.  q is rotated and rounded to f16 unscaled (the f16 tensor a
+// rotation hands to attention).  The score accumulators start at -m (m = the row's reference
+// max of the plain dot products), so S^T leaves the matrix core as (s - m), and each
+// probability is 2^((s - m) * scale * log2(e)): one multiply and one exp2.  m is set exactly
+// from a row's first tile and is otherwise left alone: the probabilities are rounded to f16
+// for the PV product, so they may grow up to the f16 range (relative precision is the same
+// at any magnitude) before anything must move.
 // A tile whose probabilities overflow f16 -- seen as an infinite row sum -- takes the
 // exact path: m moves to the tile's max, O and the running sum are rescaled and the
 // tile's probabilities are recomputed.  So the common tile costs no max reduction.
@@ -108,7 +110,7 @@ struct PrefillParams {
     int units;   // work units in all: n * hkv * wpk
     int xcd;     // grid size is a multiple of 8 (XCD-preserving snake order)
     int pairmajor; // XCD-local, pair-major unit order (KV pairs a multiple of 8; see the kernel)
-    float scale_log2;
+    float scale_log2; // scale * log2(e), applied to the fp32 scores
 };
 
 // Workgroup barrier without the release fence of __syncthreads (which would drain every
@@ -251,10 +253,10 @@ __device__ inline void rot_half_blocks(const u32x4 &a, const u32x4 &b, const flo
     yb = __builtin_bit_cast(half8, hb);
 }
 
-// q rotation, scaled and rounded to f16: the B operands of the S^T product.  The lane
+// q rotation (times the attention factor mscale) rounded to f16: the B operands of the S^T product.  The lane
 // holds dims 16 s + 8 hh .. + 7 of its query in qin[s].  Adjacent pairs: slot
 // 8 s + 4 hh + m is the lane's word m of block s.  Half-split (H16 = n_pairs / 16; the
-// rotated dims start at block 8 - 2 H16): a block below that is scaled per slot as
+// rotated dims start at block 8 - 2 H16): a block below that is taken per slot as
 // above; block s of the first rotated half and block s + H16 hold the two dims of slots
 // off / 2 + 16 (s - (8 - 2 H16)) + 8 hh + e.
 template <int H16, bool TAB>
@@ -360,7 +362,7 @@ __device__ inline void rotate_q_tab_t(half8 (&qop)[8], const u32x4 (&qin)[8], co
 template <int H16, bool TAB>
 __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char *lds, const double *wdim,
                                                      const float *sdim, int u, int g, int wk, int hist,
-                                                     int tu, const QRot rot)
+                                                     int tu, const QRot rot, float sl2)
 {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -418,6 +420,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
             const half8 a = *reinterpret_cast<const half8 *>(lds + (32 * sb + c) * ROWB + (((2 * st + hh) ^ kswz(c)) << 4));
             sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[st], sacc[sb], 0, 0, 0);
         }
+        // running max of the plain dot products; the scale enters each exp2 argument
         const int lim = qlimit - kb - 4 * hh;
         float mx = -INFINITY;
 #pragma unroll
@@ -432,7 +435,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
         mx = half_max(mx);
         if (mx > m_run) {
             // (the first tile holds key 0, visible to every row, so mx is finite)
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_run - mx) * sl2);
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
@@ -445,8 +448,8 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int r = 8 * (x & 1) + 2 * jj;
-                const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r] - m_run),
-                                    __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1] - m_run)};
+                const floatx2 pf = {__builtin_amdgcn_exp2f((sacc[x >> 1][r] - m_run) * sl2),
+                                    __builtin_amdgcn_exp2f((sacc[x >> 1][r + 1] - m_run) * sl2)};
                 l_run += pf[0] + pf[1];
                 pw[x][jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, half2v));
             }
@@ -510,10 +513,9 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     if (tid < (kMaxRopeSets + 1) * kMaxPairs) {
         const int rs = tid / kMaxPairs, dp = tid % kMaxPairs;
         const bool rot_t = 2 * dp >= tab.off;
-        const float sl2 = p.scale_log2;
         if (rs < tab.nsets) {
             wdim[rs][dp] = rot_t ? tab.sgn * tab.wrev[rs][dp - (tab.off >> 1)] : 0.0;
-            sdim[rs][dp] = rot_t ? (float)tab.mscale[rs] * sl2 : sl2;
+            sdim[rs][dp] = rot_t ? (float)tab.mscale[rs] : 1.f;
         } else {
             wdim[rs][dp] = __builtin_nan("");
             sdim[rs][dp] = __builtin_nanf("");
@@ -646,7 +648,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         if (ntiles > 1)
             issue_k(1, lds_base + TILE_B);
 
-        // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), scale, round to f16.
+        // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), round to f16.
         // When the unit's items span at most two token blocks, the workgroup computes each
         // (token, pair) factor once into LDS instead of once per query head.
         half8 qop[8];
@@ -675,9 +677,10 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // of the result sum query n and odd rows query n + 16.  Lane l finds its query's sum
         // in slot (l / 16) % 2.
         floatx4 lsum;
-        float m_run = 0.f; // reference max (log2 units)
+        float m_run = 0.f; // reference max of the dot products
+        const float sl2 = p.scale_log2;
         bool first = true;
-        floatx16 sacc[2];  // S^T of the current tile, as (score - m_run)
+        floatx16 sacc[2];  // S^T of the current tile, as (dot product - m_run)
         u32x4 pw[4];       // f16 probabilities of the previous tile (PV B operands)
         const _Float16 sel1 = (lane & 1) == ((lane >> 4) & 1) ? (_Float16)1.f : (_Float16)0.f;
         const half8 sel = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
@@ -794,8 +797,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int r = 8 * (x & 1) + 2 * jj;
-                    const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r]),
-                                        __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1])};
+                    const floatx2 pf = {__builtin_amdgcn_exp2f(sacc[x >> 1][r] * sl2),
+                                        __builtin_amdgcn_exp2f(sacc[x >> 1][r + 1] * sl2)};
                     pw[x][jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, half2v));
                 }
             }
@@ -905,7 +908,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         wg_barrier();
         if (ovf_unit == v) {
             // (without tables the rotation needs nothing beyond LDS: no live kernel arguments)
-            exact_unit<H16, TAB>(p, lds, wd, sd, u, g, wk, hist, tu, TAB ? rot : QRot{});
+            exact_unit<H16, TAB>(p, lds, wd, sd, u, g, wk, hist, tu, TAB ? rot : QRot{}, sl2);
             continue;
         }
 
@@ -917,9 +920,15 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const float inv = 1.f / lrow;
         char *ostage = lds + (wave < 4 ? 2 * TILE_B + wave * (QB * ROWB)
                                        : VREG_B + 2 * TILE_B + (wave - 4) * (QB * ROWB));
+        // the per-lane staging addresses below are recomputed per unit from an opaque copy of
+        // the lane index, so that they are not hoisted to the kernel's start and kept (or
+        // spilled) across the tile loop
+        int le = lane;
+        asm volatile("" : "+v"(le));
+        const int ce = le & 31, he = le >> 5;
         // chunk k of row c: the per-lane base with bits 4-7 flipped by k (opaque, so the
         // sixteen addresses are not hoisted out of the unit loop into spilled registers)
-        uint32_t wbase = (uint32_t)((ostage - lds) + c * ROWB + ((c & 15) << 4) + hh * 8);
+        uint32_t wbase = (uint32_t)((ostage - lds) + ce * ROWB + ((ce & 15) << 4) + he * 8);
         asm volatile("" : "+v"(wbase));
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
@@ -938,8 +947,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // first store; the asm statements keep the compiler from hoisting per-row values
         // out of the unit loop (into spilled registers) or sinking reads into the stores'
         // branches.
-        uint32_t rbase = (uint32_t)((ostage - lds) + (lane >> 4) * ROWB + (((lane & 15) ^ (lane >> 4)) << 4));
-        uint32_t olane = (uint32_t)((lane >> 4) * p.hq * ROWB + 16 * (lane & 15));
+        uint32_t rbase = (uint32_t)((ostage - lds) + (le >> 4) * ROWB + (((le & 15) ^ (le >> 4)) << 4));
+        uint32_t olane = (uint32_t)((le >> 4) * p.hq * ROWB + 16 * (le & 15));
         asm volatile("" : "+v"(rbase), "+v"(olane));
         u32x4 orows[QB / 4];
 #pragma unroll
@@ -953,7 +962,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
 #pragma unroll
         for (int x = 0; x < QB / 4; ++x) {
             char *rows4 = reinterpret_cast<char *>(p.out + (((int64_t)u * p.t + i0 + 4 * x) * p.hq + h) * kHeadDim);
-            if (wave_valid && i0 + 4 * x + (lane >> 4) < tu)
+            if (wave_valid && i0 + 4 * x + (le >> 4) < tu)
                 *reinterpret_cast<u32x4 *>(rows4 + olane) = orows[x];
         }
     } // work units

@@ -44,6 +44,17 @@ def check_attention(gpu_bits: np.ndarray, ref64: np.ndarray, what: str = "out"):
     return max_abs, row_rel
 
 
+def error_profile(gpu_bits: np.ndarray, ref64: np.ndarray) -> dict:
+    """Where the largest error sits: its index and the reference magnitude there."""
+    g = bits_to_f64(gpu_bits)
+    err = np.abs(g - ref64)
+    if not err.size:
+        return {"ref_at_max_abs": 0.0, "where": None}
+    i = int(np.argmax(err))
+    return {"ref_at_max_abs": float(np.abs(ref64.reshape(-1)[i])),
+            "where": tuple(int(x) for x in np.unravel_index(i, err.shape))}
+
+
 def check_k_rows(gpu_bits: np.ndarray, ref_bits: np.ndarray, ref64: np.ndarray, what="k"):
     """Rotated K rows: bit-exact except on an fp64-unresolvable rounding boundary."""
     mism = gpu_bits != ref_bits

@@ -62,9 +62,10 @@ def check_untouched(cache, cache0, lens_dev, t, what, chunk=16):
         assert not bool(bad.any()), f"{what}: cache rows outside the appended ones changed"
 
 
-def report(cfg, max_abs, row_rel, kb, rows):
-    print(f"{cfg.name}: {rows} output rows (all), max abs {max_abs:.2e}, row-rel {row_rel:.2e}, "
-          f"K boundary cases {kb}", flush=True)
+def report(cfg, max_abs, row_rel, kb, rows, prof):
+    print(f"{cfg.name}: {rows} output rows (all), max abs {max_abs:.2e} (at |ref| "
+          f"{prof['ref_at_max_abs']:.3f}, index {prof['where']}), "
+          f"row-rel {row_rel:.2e}, K boundary cases {kb}", flush=True)
 
 
 def run_prefill(kv, cfg):
@@ -85,6 +86,7 @@ def run_prefill(kv, cfg):
     _, ref64, k64 = oracle.prefill_kv(host["q"], host["k"], host["v"], pos, rk, rv, lens, cfg.scale,
                                       ora_rope(cfg.rope))
     max_abs, row_rel = P.check_attention(bits(out), ref64, cfg.name)
+    prof = P.error_profile(bits(out), ref64)
     t = cfg.t
     gk = bits(appended_rows(inp.cache_k, inp.lens, t))
     gv = bits(appended_rows(inp.cache_v, inp.lens, t))
@@ -95,7 +97,7 @@ def run_prefill(kv, cfg):
     kb = P.check_k_rows(gk, ok_rows, k64, cfg.name + " appended K")
     check_untouched(inp.cache_k, ck0, inp.lens, t, cfg.name + " K")
     check_untouched(inp.cache_v, cv0, inp.lens, t, cfg.name + " V")
-    report(cfg, max_abs, row_rel, kb, n * t * cfg.hq)
+    report(cfg, max_abs, row_rel, kb, n * t * cfg.hq, prof)
 
 
 def run_decode(kv, cfg, units_per_oracle_call=None):
@@ -120,6 +122,7 @@ def run_decode(kv, cfg, units_per_oracle_call=None):
     check_untouched(inp.cache_v, cv0, inp.lens, 1, cfg.name + " V")
     del ck0, cv0
     max_abs = row_rel = 0.0
+    prof = {"ref_at_max_abs": 0.0, "where": None}
     kb = 0
     for i, u0 in enumerate(range(0, n, step)):
         u1 = min(n, u0 + step)
@@ -128,13 +131,17 @@ def run_decode(kv, cfg, units_per_oracle_call=None):
                                       lens[u0:u1], cfg.scale, ora_rope(cfg.rope))
         what = f"{cfg.name} units {u0}..{u1 - 1}"
         a, r = P.check_attention(got[u0:u1], ref64, what)
+        pr = P.error_profile(got[u0:u1], ref64)
+        if a >= max_abs and pr["where"] is not None:
+            prof = {"ref_at_max_abs": pr["ref_at_max_abs"],
+                    "where": (pr["where"][0] + u0,) + pr["where"][1:]}
         max_abs, row_rel = max(max_abs, a), max(row_rel, r)
         ok_rows = np.stack([rk[u - u0][:, lens[u]] for u in range(u0, u1)])
         ov_rows = np.stack([rv[u - u0][:, lens[u]] for u in range(u0, u1)])
         assert np.array_equal(gv[u0:u1], ov_rows), f"{what}: appended V rows differ"
         kb += P.check_k_rows(gk[u0:u1], ok_rows, k64, what + " appended K")
         host_ck[i] = host_cv[i] = None
-    report(cfg, max_abs, row_rel, kb, n * cfg.hq)
+    report(cfg, max_abs, row_rel, kb, n * cfg.hq, prof)
 
 
 @pytest.mark.timeout(300)
