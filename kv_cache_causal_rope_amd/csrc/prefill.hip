@@ -73,12 +73,23 @@ namespace {
 
 constexpr int KT = 64;                 // keys per tile
 constexpr int QB = 32;                 // query tokens per wave
-constexpr int NW = 8;                  // waves per workgroup
-constexpr int NT = NW * 64;            // threads per workgroup
 constexpr int ROWB = kHeadDim * 2;     // bytes per K / V row
 constexpr int TILE_B = KT * ROWB;      // 16 KB per tensor per stage
-constexpr int NSTAGE = 4;
-constexpr int VREG_B = NSTAGE * TILE_B; // V regions start after the four K regions
+
+// The two workgroup layouts:
+//   PP (ping-pong): 8 waves in two groups a phase apart, a 4-stage ring, one workgroup per
+//       compute unit -- for long units (history at least as long as the new tokens);
+//   !PP: 4 waves in lock-step, a 2-stage ring, two workgroups per compute unit whose waves
+//       share the SIMDs -- for short units, whose prologue and epilogue the other
+//       workgroup's tile loop then covers.
+template <bool PP> struct Lay {
+    static constexpr int NW = PP ? 8 : 4;          // waves per workgroup
+    static constexpr int NT = NW * 64;             // threads per workgroup
+    static constexpr int NSTAGE = PP ? 4 : 2;      // LDS stages, a K and a V tile each
+    static constexpr int VREG_B = NSTAGE * TILE_B; // V regions start after the K regions
+    static constexpr int ROWS = KT / NW;           // rows of a tile one wave moves
+    static constexpr int NDMA = ROWS / 4;          // DMA instructions per wave and tile
+};
 constexpr int RD = 6;                  // operand reads in flight ahead of the MFMAs
 
 // How q is rotated beyond the per-slot angle rates and scales kept in LDS.  Slot dp of a
@@ -151,9 +162,10 @@ __device__ inline uint32_t lds_offset(const void *p)
 }
 
 // Per-lane byte offsets of the K rows a lane moves into LDS: wave w moves rows
-// 8w .. 8w+7, 4 rows per instruction, lane L taking row 4i + L/16 of its group and the
-// global chunk that lands in LDS chunk L % 16 of that row.
-__device__ inline int krow(int wave, int lane, int i) { return 8 * wave + 4 * i + (lane >> 4); }
+// ROWS w .. ROWS (w + 1) - 1, 4 rows per instruction, lane L taking row 4i + L/16 of its
+// group and the global chunk that lands in LDS chunk L % 16 of that row.
+template <bool PP>
+__device__ inline int krow(int wave, int lane, int i) { return Lay<PP>::ROWS * wave + 4 * i + (lane >> 4); }
 __device__ inline uint32_t koffset(int row, int lane)
 {
     return (uint32_t)(row * ROWB + (((lane & 15) ^ kswz(row)) << 4));
@@ -165,10 +177,11 @@ __device__ inline uint32_t koffset(int row, int lane)
 // which 16 dims of the block), lane 4 j + r addresses key row 16 x + 4 hh + j, dims
 // 32 db + 16 (gq % 2) + 4 r .. + 3, i.e. chunk 4 db + 2 (gq % 2) + r / 2 swizzled to
 // 4 (db ^ j) + 2 (gq % 2) + r / 2.
+template <bool PP>
 __device__ inline uint32_t vt_base(int lane)
 {
     const int hh = lane >> 5, j = (lane >> 2) & 3, r = lane & 3;
-    return (uint32_t)(VREG_B + (4 * hh + j) * ROWB + 64 * j + 32 * ((lane >> 4) & 1) + 8 * r);
+    return (uint32_t)(Lay<PP>::VREG_B + (4 * hh + j) * ROWB + 64 * j + 32 * ((lane >> 4) & 1) + 8 * r);
 }
 
 // V^T operand of key step x, dim block db from the stage at byte offset so
@@ -192,12 +205,14 @@ __device__ inline const char *uniform_ptr(const char *ptr)
 // K rows of one tile straight into an LDS stage.  `tile` is the wave-uniform address of
 // the tile's first row; the loads are inline asm so the compiler does not track them;
 // they are waited for explicitly (vmcnt) before the barrier that publishes the stage.
-__device__ inline void dma_k(const char *tile, const uint32_t (&off)[2], uint32_t stage_lds, int wave)
+template <bool PP>
+__device__ inline void dma_k(const char *tile, const uint32_t (&off)[Lay<PP>::NDMA], uint32_t stage_lds, int wave)
 {
     const char *t = uniform_ptr(tile);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)((8 * wave + 4 * i) * ROWB));
+    for (int i = 0; i < Lay<PP>::NDMA; ++i) {
+        const uint32_t dst =
+            __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)((Lay<PP>::ROWS * wave + 4 * i) * ROWB));
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
                      : "s"(dst), "v"(off[i]), "s"(t)
@@ -359,11 +374,12 @@ __device__ inline void rotate_q_tab_t(half8 (&qop)[8], const u32x4 (&qin)[8], co
 // max moved on every tile that exceeds it (so no probability exceeds 1): plainly, one
 // tile at a time through LDS stage 0, each wave its own item.  Not inlined, so that its
 // registers do not weigh on the fast path.
-template <int H16, bool TAB>
+template <int H16, bool TAB, bool PP>
 __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char *lds, const double *wdim,
                                                      const float *sdim, int u, int g, int wk, int hist,
                                                      int tu, const QRot rot, float sl2)
 {
+    constexpr int NW = Lay<PP>::NW, NDMA = Lay<PP>::NDMA, VREG_B = Lay<PP>::VREG_B;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -391,7 +407,7 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     half8 qop[8];
     rotate_q_t<H16, TAB>(qop, qin, p.pos[(int64_t)u * p.t + iq], hh, wdim, sdim, rot);
 
-    const uint32_t vb = vt_base(lane);
+    const uint32_t vb = vt_base<PP>(lane);
     floatx16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -400,16 +416,16 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
     for (int j = 0; j < ntiles; ++j) {
         const int kb = j * KT;
         // K and V rows (clamped past kend) straight into stage 0
-        uint32_t ko[2], vo[2];
+        uint32_t ko[NDMA], vo[NDMA];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int row = krow(wave, lane, r);
+        for (int r = 0; r < NDMA; ++r) {
+            const int row = krow<PP>(wave, lane, r);
             ko[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
             vo[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ vswz(row)) << 4));
         }
         const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
-        dma_k(uniform_ptr(kbase + (int64_t)kb * ROWB), ko, lds0, wave);
-        dma_k(uniform_ptr(vbase + (int64_t)kb * ROWB), vo, lds0 + VREG_B, wave);
+        dma_k<PP>(uniform_ptr(kbase + (int64_t)kb * ROWB), ko, lds0, wave);
+        dma_k<PP>(uniform_ptr(vbase + (int64_t)kb * ROWB), vo, lds0 + VREG_B, wave);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         wg_barrier();
 
@@ -480,9 +496,12 @@ __device__ __attribute__((noinline)) void exact_unit(const PrefillParams p, char
 // H16: the pairing of q's rotated dims, as in rotate_q_t; TAB: factors from the caller's
 // tables.  One kernel per variant keeps the other variants' code out of the fast path's
 // register allocation.
-template <int H16, bool TAB>
-__global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeTable tab, QRot rot)
+template <int H16, bool TAB, bool PP>
+__global__ void __launch_bounds__(Lay<PP>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_attn_kernel(PrefillParams p, RopeTable tab, QRot rot)
 {
+    constexpr int NW = Lay<PP>::NW, NT = Lay<PP>::NT, NSTAGE = Lay<PP>::NSTAGE, VREG_B = Lay<PP>::VREG_B,
+                  NDMA = Lay<PP>::NDMA;
     __shared__ __align__(16) char lds[2 * NSTAGE * TILE_B];
     // per parameter set (row kMaxRopeSets: NaN, for an invalid set index): revolutions per
     // position of dim pair dp (0: unrotated) and its output scale
@@ -510,8 +529,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
     const int P = gridDim.x;
 
     // rotation tables of every parameter set, shared by every unit
-    if (tid < (kMaxRopeSets + 1) * kMaxPairs) {
-        const int rs = tid / kMaxPairs, dp = tid % kMaxPairs;
+    for (int e = tid; e < (kMaxRopeSets + 1) * kMaxPairs; e += NT) {
+        const int rs = e / kMaxPairs, dp = e % kMaxPairs;
         const bool rot_t = 2 * dp >= tab.off;
         if (rs < tab.nsets) {
             wdim[rs][dp] = rot_t ? tab.sgn * tab.wrev[rs][dp - (tab.off >> 1)] : 0.0;
@@ -586,10 +605,10 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const char *vbase = reinterpret_cast<const char *>(p.cv + ((int64_t)u * p.hkv + g) * p.s_cap * kHeadDim);
 
         // per-lane tile offsets (full tiles) and the LDS addresses of this thread
-        uint32_t koff[2], voff[2];
+        uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int row = krow(wave, lane, r);
+        for (int r = 0; r < NDMA; ++r) {
+            const int row = krow<PP>(wave, lane, r);
             koff[r] = koffset(row, lane);
             voff[r] = (uint32_t)(row * ROWB + (((lane & 15) ^ vswz(row)) << 4));
         }
@@ -601,16 +620,16 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             const int kb = j * KT;
             const char *tile = kbase + (int64_t)kb * ROWB;
             if (kb + KT <= kend) {
-                dma_k(tile, koff, stage_lds, wave);
+                dma_k<PP>(tile, koff, stage_lds, wave);
             } else {
                 // the source row clamps; the swizzled chunk stays the destination row's
-                uint32_t o[2];
+                uint32_t o[NDMA];
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int row = krow(wave, lane, r);
+                for (int r = 0; r < NDMA; ++r) {
+                    const int row = krow<PP>(wave, lane, r);
                     o[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ kswz(row)) << 4));
                 }
-                dma_k(tile, o, stage_lds, wave);
+                dma_k<PP>(tile, o, stage_lds, wave);
             }
         };
         // V rows the same way into the V region of a stage, under their own chunk swizzle
@@ -618,15 +637,15 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             const int kb = j * KT;
             const char *tile = vbase + (int64_t)kb * ROWB;
             if (kb + KT <= kend) {
-                dma_k(tile, voff, stage_lds, wave);
+                dma_k<PP>(tile, voff, stage_lds, wave);
             } else {
-                uint32_t o[2];
+                uint32_t o[NDMA];
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int row = krow(wave, lane, r);
+                for (int r = 0; r < NDMA; ++r) {
+                    const int row = krow<PP>(wave, lane, r);
                     o[r] = (uint32_t)(min(row, klast - kb) * ROWB + (((lane & 15) ^ vswz(row)) << 4));
                 }
-                dma_k(tile, o, stage_lds, wave);
+                dma_k<PP>(tile, o, stage_lds, wave);
             }
         };
 
@@ -638,21 +657,25 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // position of this thread's token of the unit's rotation table (see below; rows
         // past t take row t - 1's), loaded first so that it arrives first
         const int ntok = (tb_last - tb_first + 1) * QB;
-        const int tpos = p.pos[(int64_t)u * p.t + min(tb_first * QB + tid % ntok, p.t - 1)];
+        const int tpos = PP ? p.pos[(int64_t)u * p.t + min(tb_first * QB + tid % ntok, p.t - 1)] : 0;
         u32x4 qin[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
             qin[s] = ld16(qrow + 16 * s + 8 * hh);
+        if (!PP)
+            wg_barrier(); // every wave has read its previous unit's output rows back (K region)
         issue_k(0, lds_base);
         issue_v(0, lds_base + VREG_B);
         if (ntiles > 1)
             issue_k(1, lds_base + TILE_B);
 
         // ---- q prologue: rotate (fp32 trig of the fp64-reduced angle), round to f16.
-        // When the unit's items span at most two token blocks, the workgroup computes each
-        // (token, pair) factor once into LDS instead of once per query head.
+        // In the ping-pong layout, when the unit's items span at most two token blocks, the
+        // workgroup computes each (token, pair) factor once into LDS (the K region of stages
+        // 2-3, free at this point) instead of once per query head; the lock-step layout's
+        // ring has no room for the table, and the other workgroup covers the trig.
         half8 qop[8];
-        if (ntok <= 2 * QB) {
+        if (PP && ntok <= 2 * QB) {
             wg_barrier(); // every wave has read its previous unit's output rows back
             fill_rot_table<TAB>(lds, tpos, ntok, tid, wd, sd, rot);
             wg_barrier();
@@ -666,7 +689,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // sits in bits 5-7 of the byte offset, so one per-lane base serves all eight steps
         // through an xor.  V^T operands: vt_base.
         const uint32_t kbase0 = (uint32_t)(c * ROWB + ((hh ^ kswz(c)) << 4));
-        const uint32_t vbase0 = vt_base(lane);
+        const uint32_t vbase0 = vt_base<PP>(lane);
 
         floatx16 o[4];
         // row sums of the f16 probabilities, accumulated on the matrix core by one
@@ -685,12 +708,9 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         const _Float16 sel1 = (lane & 1) == ((lane >> 4) & 1) ? (_Float16)1.f : (_Float16)0.f;
         const half8 sel = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
 
-        // Ping-pong: a wave's phases alternate
+        // A wave's phases alternate
         //   M(j): PV of tile j-1, then S^T of tile j   (32 MFMAs)
         //   S(j): softmax of tile j                     (VALU)
-        // Tile j sits in LDS stage j % 4 from two tiles before its first use (S^T in M(j))
-        // until its last (PV in M(j+1) of the trailing group).
-        const int grp = wave >> 2;
         auto tile_active = [&](int j) { return wave_valid && j * KT < kend_w; };
 
         // The operand reads of an M phase, x = 0 .. 31: x < 16 the V^T blocks of tile j-1
@@ -760,35 +780,6 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
         };
 
-        // Tile staging for M(j) (STG = j % 4): wait for this wave's share of the previous
-        // staging's loads (K of tile j+1, V of tile j), which the barrier ending the phase
-        // then publishes, and start the next: K of tile j+2 and V of tile j+1, each into its
-        // stage.  It runs at the end of the softmax phase before M(j), while the SIMD
-        // partner is in its MFMA phase.  A V stage is refilled one phase pair after its K
-        // stage: V of tile j-3 is read by the PV part of M(j-2), which the trailing group
-        // runs during the leading group's softmax phase S(j-2).
-        auto stage_tiles = [&](auto stg_c, int j) {
-            constexpr int STG = decltype(stg_c)::value;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            if (j + 2 < ntiles)
-                issue_k(j + 2, lds_base + (uint32_t)(((STG + 2) % NSTAGE) * TILE_B));
-            if (j + 1 < ntiles)
-                issue_v(j + 1, lds_base + (uint32_t)(VREG_B + ((STG + 1) % NSTAGE) * TILE_B));
-        };
-
-        // M(j), 1 <= j < ntiles: PV of tile j-1 and S^T of tile j.  A wave whose tile j-1 is
-        // past its last key runs it anyway on zero probabilities (its SIMD partner is in
-        // its softmax, so the matrix core is free), which keeps one code path.
-        auto phase_m = [&](auto stg_c, int j) {
-            constexpr int STG = decltype(stg_c)::value;
-            // the matrix-core phase outranks the other group's softmax for issue slots
-            __builtin_amdgcn_s_setprio(1);
-            mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{}, std::true_type{},
-                    STG * TILE_B, ((STG + NSTAGE - 1) % NSTAGE) * TILE_B);
-            __builtin_amdgcn_s_setprio(0);
-            wg_barrier();
-        };
-
         // probabilities of the tile (f16 pairs, the PV operand) and their sum
         // probabilities of the tile (f16 pairs, the PV operand)
         auto probs = [&]() {
@@ -830,10 +821,8 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             }
         };
 
-        // S(j) (STG = j % 4): softmax of tile j, then the staging and the first operand
-        // reads (V^T of tile j) of M(j+1).
-        auto phase_s = [&](auto stg_c, int j) {
-            constexpr int STG = decltype(stg_c)::value;
+        // softmax of tile j into pw (zero probabilities for a wave past its last key)
+        auto softmax = [&](int j) {
             if (tile_active(j)) {
                 mask_tile(j);
                 if (first) {
@@ -851,9 +840,6 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
                 for (int x = 0; x < 4; ++x)
                     pw[x] = u32x4{0u};
             }
-            stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
-            prefetch(STG * TILE_B);
-            wg_barrier_reads_in_flight<2 * RD>(); // two transposing reads per V^T operand
         };
 
 #pragma unroll
@@ -861,43 +847,138 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
             o[db] = floatx16{0.f};
         lsum = floatx4{0.f};
 
-        // tile 0 (K and V) in stage 0, K of tile 1 in stage 1
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        wg_barrier();
+        if constexpr (PP) {
+            // Ping-pong: waves 0-3 and 4-7 run the same phases, the second group one phase
+            // behind, each phase ending in a workgroup barrier.  Tile j sits in LDS stage
+            // j % 4 from two tiles before its first use (S^T in M(j)) until its last (PV in
+            // M(j+1) of the trailing group).
+            const int grp = wave >> 2;
+            // Tile staging for M(j) (STG = j % 4): wait for this wave's share of the previous
+            // staging's loads (K of tile j+1, V of tile j), which the barrier ending the phase
+            // then publishes, and start the next: K of tile j+2 and V of tile j+1, each into its
+            // stage.  It runs at the end of the softmax phase before M(j), while the SIMD
+            // partner is in its MFMA phase.  A V stage is refilled one phase pair after its K
+            // stage: V of tile j-3 is read by the PV part of M(j-2), which the trailing group
+            // runs during the leading group's softmax phase S(j-2).
+            auto stage_tiles = [&](auto stg_c, int j) {
+                constexpr int STG = decltype(stg_c)::value;
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (j + 2 < ntiles)
+                    issue_k(j + 2, lds_base + (uint32_t)(((STG + 2) % NSTAGE) * TILE_B));
+                if (j + 1 < ntiles)
+                    issue_v(j + 1, lds_base + (uint32_t)(VREG_B + ((STG + 1) % NSTAGE) * TILE_B));
+            };
 
-        if (grp == 1)
-            wg_barrier(); // the trailing group starts one phase late
-        // M(0): S^T of tile 0 only
-        stage_tiles(std::integral_constant<int, 0>{}, 0);
-        __builtin_amdgcn_s_setprio(1);
-        mstream(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{}, std::false_type{}, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
-        wg_barrier();
-        phase_s(std::integral_constant<int, 0>{}, 0);
-        for (int j0 = 1; j0 < ntiles; j0 += 4) {
-            phase_m(std::integral_constant<int, 1>{}, j0);
-            phase_s(std::integral_constant<int, 1>{}, j0);
-            if (j0 + 1 < ntiles) {
-                phase_m(std::integral_constant<int, 2>{}, j0 + 1);
-                phase_s(std::integral_constant<int, 2>{}, j0 + 1);
-                if (j0 + 2 < ntiles) {
-                    phase_m(std::integral_constant<int, 3>{}, j0 + 2);
-                    phase_s(std::integral_constant<int, 3>{}, j0 + 2);
-                    if (j0 + 3 < ntiles) {
-                        phase_m(std::integral_constant<int, 0>{}, j0 + 3);
-                        phase_s(std::integral_constant<int, 0>{}, j0 + 3);
+            // M(j), 1 <= j < ntiles: PV of tile j-1 and S^T of tile j.  A wave whose tile j-1 is
+            // past its last key runs it anyway on zero probabilities (its SIMD partner is in
+            // its softmax, so the matrix core is free), which keeps one code path.
+            auto phase_m = [&](auto stg_c, int j) {
+                constexpr int STG = decltype(stg_c)::value;
+                // the matrix-core phase outranks the other group's softmax for issue slots
+                __builtin_amdgcn_s_setprio(1);
+                mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{}, std::true_type{},
+                        STG * TILE_B, ((STG + NSTAGE - 1) % NSTAGE) * TILE_B);
+                __builtin_amdgcn_s_setprio(0);
+                wg_barrier();
+            };
+
+            // S(j) (STG = j % 4): softmax of tile j, then the staging and the first operand
+            // reads (V^T of tile j) of M(j+1).
+            auto phase_s = [&](auto stg_c, int j) {
+                constexpr int STG = decltype(stg_c)::value;
+                softmax(j);
+                stage_tiles(std::integral_constant<int, (STG + 1) % NSTAGE>{}, j + 1);
+                prefetch(STG * TILE_B);
+                wg_barrier_reads_in_flight<2 * RD>(); // two transposing reads per V^T operand
+            };
+
+            // tile 0 (K and V) in stage 0, K of tile 1 in stage 1
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wg_barrier();
+
+            if (grp == 1)
+                wg_barrier(); // the trailing group starts one phase late
+            // M(0): S^T of tile 0 only
+            stage_tiles(std::integral_constant<int, 0>{}, 0);
+            __builtin_amdgcn_s_setprio(1);
+            mstream(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{}, std::false_type{}, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
+            wg_barrier();
+            phase_s(std::integral_constant<int, 0>{}, 0);
+            for (int j0 = 1; j0 < ntiles; j0 += 4) {
+                phase_m(std::integral_constant<int, 1>{}, j0);
+                phase_s(std::integral_constant<int, 1>{}, j0);
+                if (j0 + 1 < ntiles) {
+                    phase_m(std::integral_constant<int, 2>{}, j0 + 1);
+                    phase_s(std::integral_constant<int, 2>{}, j0 + 1);
+                    if (j0 + 2 < ntiles) {
+                        phase_m(std::integral_constant<int, 3>{}, j0 + 2);
+                        phase_s(std::integral_constant<int, 3>{}, j0 + 2);
+                        if (j0 + 3 < ntiles) {
+                            phase_m(std::integral_constant<int, 0>{}, j0 + 3);
+                            phase_s(std::integral_constant<int, 0>{}, j0 + 3);
+                        }
                     }
                 }
             }
+            // M(ntiles): PV of the last tile only (its first reads were issued by S(ntiles-1))
+            __builtin_amdgcn_s_setprio(1);
+            mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{}, std::true_type{}, 0,
+                    ((ntiles - 1) % NSTAGE) * TILE_B);
+            __builtin_amdgcn_s_setprio(0);
+            wg_barrier();
+            if (grp == 0)
+                wg_barrier(); // same barrier count for both groups
+        } else {
+            // Lock-step: the four waves run the same phase; the other workgroup on the compute
+            // unit supplies the overlap of matrix and vector work.  One barrier per tile, in
+            // S(j) after this wave's wait for its share of K(j+1) and V(j): it publishes them,
+            // and every wave is then past M(j).  Then K of tile j+2 goes into K stage j % 2
+            // (K(j) was last read by M(j)'s S^T part) and V of tile j+1 into V stage
+            // (j+1) % 2 (V(j-1) was last read by M(j)'s PV part).
+            auto phase_s = [&](auto stg_c, int j) {
+                constexpr int STG = decltype(stg_c)::value;
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                wg_barrier();
+                if (j + 2 < ntiles)
+                    issue_k(j + 2, lds_base + (uint32_t)(STG * TILE_B));
+                if (j + 1 < ntiles)
+                    issue_v(j + 1, lds_base + (uint32_t)(VREG_B + (STG ^ 1) * TILE_B));
+                softmax(j);
+                prefetch(STG * TILE_B); // V^T of tile j, for M(j+1)
+            };
+            // M(j), 1 <= j < ntiles (STG = j % 2): PV of tile j-1 and S^T of tile j
+            auto phase_m = [&](auto stg_c, int j) {
+                constexpr int STG = decltype(stg_c)::value;
+                (void)j;
+                __builtin_amdgcn_s_setprio(1);
+                mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 32>{}, std::true_type{},
+                        STG * TILE_B, (STG ^ 1) * TILE_B);
+                __builtin_amdgcn_s_setprio(0);
+            };
+
+            // tile 0 (K and V) in stage 0, K of tile 1 in stage 1
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wg_barrier();
+            // M(0): S^T of tile 0 only
+            __builtin_amdgcn_s_setprio(1);
+            mstream(std::integral_constant<int, 16>{}, std::integral_constant<int, 32>{}, std::false_type{}, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
+            phase_s(std::integral_constant<int, 0>{}, 0);
+            for (int j0 = 1; j0 < ntiles; j0 += 2) {
+                phase_m(std::integral_constant<int, 1>{}, j0);
+                phase_s(std::integral_constant<int, 1>{}, j0);
+                if (j0 + 1 < ntiles) {
+                    phase_m(std::integral_constant<int, 0>{}, j0 + 1);
+                    phase_s(std::integral_constant<int, 0>{}, j0 + 1);
+                }
+            }
+            // M(ntiles): PV of the last tile only
+            __builtin_amdgcn_s_setprio(1);
+            mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{}, std::true_type{}, 0,
+                    ((ntiles - 1) % NSTAGE) * TILE_B);
+            __builtin_amdgcn_s_setprio(0);
         }
-        // M(ntiles): PV of the last tile only (its first reads were issued by S(ntiles-1))
-        __builtin_amdgcn_s_setprio(1);
-        mstream(std::integral_constant<int, 0>{}, std::integral_constant<int, 16>{}, std::true_type{}, 0,
-                ((ntiles - 1) % NSTAGE) * TILE_B);
-        __builtin_amdgcn_s_setprio(0);
-        wg_barrier();
-        if (grp == 0)
-            wg_barrier(); // same barrier count for both groups
 
         // An f16 probability past its range made a row sum infinite (or a NaN input made
         // it NaN): the workgroup recomputes the unit on the exact path.  The flag holds the
@@ -908,7 +989,7 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         wg_barrier();
         if (ovf_unit == v) {
             // (without tables the rotation needs nothing beyond LDS: no live kernel arguments)
-            exact_unit<H16, TAB>(p, lds, wd, sd, u, g, wk, hist, tu, TAB ? rot : QRot{}, sl2);
+            exact_unit<H16, TAB, PP>(p, lds, wd, sd, u, g, wk, hist, tu, TAB ? rot : QRot{}, sl2);
             continue;
         }
 
@@ -918,8 +999,12 @@ __global__ void __launch_bounds__(NT) prefill_attn_kernel(PrefillParams p, RopeT
         // that every global store writes whole 256-byte rows instead of 8-byte pieces of 64
         // rows.  16-byte chunk k of row c sits at chunk k ^ (c % 16).
         const float inv = 1.f / lrow;
-        char *ostage = lds + (wave < 4 ? 2 * TILE_B + wave * (QB * ROWB)
-                                       : VREG_B + 2 * TILE_B + (wave - 4) * (QB * ROWB));
+        // (ping-pong: stages 2-3, idle from the last barrier until the next unit's first K
+        // tile 2 load; lock-step: the K region, last read by M(ntiles-1), refilled only after
+        // the next unit's first barrier)
+        char *ostage = lds + (!PP ? wave * (QB * ROWB)
+                              : wave < 4 ? 2 * TILE_B + wave * (QB * ROWB)
+                                         : VREG_B + 2 * TILE_B + (wave - 4) * (QB * ROWB));
         // the per-lane staging addresses below are recomputed per unit from an opaque copy of
         // the lane index, so that they are not hoisted to the kernel's start and kept (or
         // spilled) across the tile loop
@@ -994,9 +1079,14 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
     p.s_cap = s.s_cap;
     p.max_hist = s.max_hist;
     p.G = s.hq / s.hkv;
+    // Layout: ping-pong when the history is at least as long as the new tokens (long
+    // units: measured 3 % faster than lock-step on a 32-layer 3840 + 256 prefill_kv),
+    // lock-step otherwise (short units: 5-6 % faster on a 28-layer T = 1024 prefill)
+    const bool pp = s.max_hist >= s.t;
+    const int nw = pp ? Lay<true>::NW : Lay<false>::NW;
     const int tblocks = (s.t + QB - 1) / QB;
     p.items = tblocks * p.G;
-    p.wpk = (p.items + NW - 1) / NW;
+    p.wpk = (p.items + nw - 1) / nw;
     const int64_t units = (int64_t)s.n * s.hkv * p.wpk;
     if (units > INT32_MAX)
         return hipErrorInvalidValue;
@@ -1010,30 +1100,39 @@ hipError_t launch_prefill_attention(const uint16_t *q, const uint16_t *cache_k,
     rot.off2 = tab.off >> 1;
     rot.h16 = tab.half ? tab.n_pairs / 16 : 0;
     rot.sgn = (float)tab.sgn;
-    // one workgroup per compute unit (the LDS ring takes most of a CU's LDS)
+    // one ping-pong workgroup per compute unit (its ring takes most of a CU's LDS), or two
+    // lock-step ones
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess)
         e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess)
         return e;
-    const int64_t blocks = std::min<int64_t>(units, std::max(ncu, 1));
+    const int64_t blocks = std::min<int64_t>(units, (int64_t)std::max(ncu, 1) * (pp ? 1 : 2));
     p.xcd = (blocks % 8 == 0) ? 1 : 0;
     // pair-major order when the history bounds the work per unit (the units of a pair then
     // differ by at most t keys of their max_hist + t): measured 2-3 % faster on a 32-layer
     // 3840 + 256 prefill_kv, 1-2 % slower on a T = 1024 prefill
-    p.pairmajor = (p.xcd && (s.n * s.hkv) % 8 == 0 && s.max_hist >= s.t) ? 1 : 0;
+    p.pairmajor = (pp && p.xcd && (s.n * s.hkv) % 8 == 0) ? 1 : 0;
 
     if (ev_before)
         (void)hipEventRecord(ev_before, stream);
     using Kernel = void (*)(PrefillParams, RopeTable, QRot);
-    static const Kernel kernels[2][5] = {
-        {prefill_attn_kernel<0, false>, prefill_attn_kernel<1, false>, prefill_attn_kernel<2, false>,
-         prefill_attn_kernel<3, false>, prefill_attn_kernel<4, false>},
-        {prefill_attn_kernel<0, true>, prefill_attn_kernel<1, true>, prefill_attn_kernel<2, true>,
-         prefill_attn_kernel<3, true>, prefill_attn_kernel<4, true>}};
-    hipLaunchKernelGGL(kernels[tab.cos_t ? 1 : 0][rot.h16], dim3((unsigned)blocks), dim3(NT), 0, stream, p, tab,
-                       rot);
+    static const Kernel kernels[2][2][5] = {
+        {{prefill_attn_kernel<0, false, false>, prefill_attn_kernel<1, false, false>,
+          prefill_attn_kernel<2, false, false>, prefill_attn_kernel<3, false, false>,
+          prefill_attn_kernel<4, false, false>},
+         {prefill_attn_kernel<0, true, false>, prefill_attn_kernel<1, true, false>,
+          prefill_attn_kernel<2, true, false>, prefill_attn_kernel<3, true, false>,
+          prefill_attn_kernel<4, true, false>}},
+        {{prefill_attn_kernel<0, false, true>, prefill_attn_kernel<1, false, true>,
+          prefill_attn_kernel<2, false, true>, prefill_attn_kernel<3, false, true>,
+          prefill_attn_kernel<4, false, true>},
+         {prefill_attn_kernel<0, true, true>, prefill_attn_kernel<1, true, true>,
+          prefill_attn_kernel<2, true, true>, prefill_attn_kernel<3, true, true>,
+          prefill_attn_kernel<4, true, true>}}};
+    hipLaunchKernelGGL(kernels[pp ? 1 : 0][tab.cos_t ? 1 : 0][rot.h16], dim3((unsigned)blocks),
+                       dim3(pp ? Lay<true>::NT : Lay<false>::NT), 0, stream, p, tab, rot);
     hipError_t err = hipGetLastError();
     if (ev_after)
         (void)hipEventRecord(ev_after, stream);

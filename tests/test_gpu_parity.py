@@ -148,6 +148,8 @@ def test_prefill_shapes(kv, n, t, hq, hkv):
     (1, 96, 6, 6, [1000], W.PLAIN_128),
     # history >= t and 32 KV pairs: the pair-major unit order, over two rounds of the grid
     (16, 200, 32, 2, [250 + 13 * u for u in range(16)], W.PLAIN_128),
+    # history shorter than t: the lock-step layout (two workgroups per compute unit)
+    (3, 100, 32, 2, [0, 37, 90], W.PLAIN_128),
 ])
 def test_prefill_kv_shapes(kv, n, t, hq, hkv, lens, rope):
     cfg = custom(n, t, hq, hkv, max(lens) + t + 5, rope=rope, seed=300 + t)
@@ -232,11 +234,12 @@ def test_prefill_score_spike(kv, n, t, hq, hkv, lens, spike):
     check_prefill(d, out, ref, lens, t, f"score-spike prefill n{n} t{t} {hq}/{hkv} {lens}")
 
 
-def test_prefill_poisoned_tail_is_never_read(kv):
-    cfg = custom(2, 50, 12, 2, 200, seed=400)
+@pytest.mark.parametrize("t", [50, 90])  # history 70 >= t: ping-pong layout; < t: lock-step
+def test_prefill_poisoned_tail_is_never_read(kv, t):
+    cfg = custom(2, t, 12, 2, 200, seed=400 + t)
     lens = [30, 70]
     inp, d, out, ref = run_prefill_kv(kv, cfg, lens, W.PLAIN_128, poison=True)
-    check_prefill(d, out, ref, lens, 50, "prefill_kv poisoned")
+    check_prefill(d, out, ref, lens, t, f"prefill_kv t{t} poisoned")
 
 
 # ------------------------------------------------------------------ decode
