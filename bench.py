@@ -47,13 +47,13 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 2.6734e+08,
-        "src": ("e1740d62b86d7a50b16f5e21189e638be298326b5de5ca8e96eaadc9d4521b36",
+        "bytes": 2.7360e+08,
+        "src": ("1b6e24a75670c06300e54ab5d380f1b3983d3dd0900ed82fbd520039780504a4",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
     "prefill_attn:h4096_prefill_kv_3840p256": {
-        "bytes": 6.5901e+08,
-        "src": ("e1740d62b86d7a50b16f5e21189e638be298326b5de5ca8e96eaadc9d4521b36",
+        "bytes": 2.6894e+08,
+        "src": ("1b6e24a75670c06300e54ab5d380f1b3983d3dd0900ed82fbd520039780504a4",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
     "decode_attn:qwen1p5b_decode_l4096_b32": {
