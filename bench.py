@@ -57,23 +57,23 @@ TRAFFIC = {
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
     "decode_attn:qwen1p5b_decode_l4096_b32": {
-        "bytes": 2.8411e+09,
-        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+        "bytes": 2.8410e+09,
+        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
     "decode_attn:yarn_decode_l32k_b64": {
-        "bytes": 2.3069e+10,
-        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+        "bytes": 2.3068e+10,
+        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
     "decode_attn:qwen1p5b_decode_l1024_b1": {
-        "bytes": 3.0548e+07,
-        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+        "bytes": 3.0551e+07,
+        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
     "decode_attn:qwen1p5b_decode_l4096_b1": {
-        "bytes": 7.2232e+07,
-        "src": ("4da3e46872e7557f093023e5f562cba22aa44e9e0464bdceea53c51289e09db5",
+        "bytes": 7.2229e+07,
+        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
 }

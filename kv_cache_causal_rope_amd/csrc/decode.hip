@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace kvrope {
 
@@ -244,16 +245,21 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) de
     const uint32_t my_stage0 = (uint32_t)(wave * NS * STAGE_B);
 
     // tile t of the chunk (t = wave + 4 i) into stage i % NS of this wave
-    auto issue = [&](int i) {
+    // (K and V separately: with one stage per wave, the next tile's K goes out once the
+    // S^T product has read this tile's K, and its V once the PV product has read this V)
+    auto issue_t = [&](auto v_c, int i) {
+        constexpr bool ISV = decltype(v_c)::value;
         const int t = wave + NWAVES * i;
         const int kb = k0 + KT * t;
         const int last = min(KT, k1 - kb) - 1;
-        uint32_t ko[8], vo[8];
-        tile_offsets<false>(lane, last, ko);
-        tile_offsets<true>(lane, last, vo);
-        const uint32_t st = lds0 + my_stage0 + (uint32_t)((i % NS) * STAGE_B);
-        dma_tile(kslab + (int64_t)kb * ROWB, ko, st);
-        dma_tile(vslab + (int64_t)kb * ROWB, vo, st + TILE_B);
+        uint32_t of[8];
+        tile_offsets<ISV>(lane, last, of);
+        const uint32_t st = lds0 + my_stage0 + (uint32_t)((i % NS) * STAGE_B) + (ISV ? TILE_B : 0u);
+        dma_tile((ISV ? vslab : kslab) + (int64_t)kb * ROWB, of, st);
+    };
+    auto issue = [&](int i) {
+        issue_t(std::false_type{}, i);
+        issue_t(std::true_type{}, i);
     };
     const int my_tiles = wave < ntiles ? (ntiles - wave + NWAVES - 1) / NWAVES : 0;
 #pragma unroll
@@ -384,9 +390,13 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) de
         const int t = wave + NWAVES * i;
         const int kb = k0 + KT * t;
         const uint32_t st = my_stage0 + (uint32_t)((i % NS) * STAGE_B);
-        // this tile's 16 loads are done once at most the next tile's 16 are outstanding
+        // this tile's K: with more stages, done once at most the next tile's 16 loads are
+        // outstanding; with one, once at most this tile's 8 V loads are (loads complete in
+        // order, and K went out first)
         if (i + 1 < my_tiles && NS > 1)
             asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (NS == 1 && !(new_here && t == t_new))
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (new_here && t == t_new) {
@@ -415,6 +425,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) de
         for (int s = 0; s < 8; ++s) {
             const half8 a = *reinterpret_cast<const half8 *>(lds + st + (kb0 ^ (uint32_t)(s << 5)));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qop[s], sacc, 0, 0, 0);
+        }
+        if (NS == 1 && i + 1 < my_tiles) {
+            // the K stage is free once the S^T operand reads returned
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_t(std::false_type{}, i + 1);
         }
         // lane holds keys kb + 8 (r / 4) + 4 hh + r % 4 of head column c
         const int lim = k1 - kb - 4 * hh; // keys at or past k1 are masked
@@ -448,6 +463,13 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) de
                 pw[x][jj] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, half2v));
             }
         }
+        // this tile's V: with one stage, at most the next tile's 8 K loads may be outstanding
+        if (NS == 1) {
+            if (i + 1 < my_tiles)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         // O^T += V^T . P^T
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -460,7 +482,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) de
         // the stage is free once its operand reads returned (the MFMAs above consumed them)
         if (i + NS < my_tiles) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            issue(i + NS);
+            if (NS == 1)
+                issue_t(std::true_type{}, i + 1);
+            else
+                issue(i + NS);
         }
     }
 
