@@ -21,7 +21,9 @@ single-sequence decode workloads (28 layers, caches to 1024 and to 4096 rows; ex
 `decode` entries, launch-dominated).
 
 `roofline` describes the dominant kernel (the prefill flash kernel), timed per launch
-with HIP events the library records around it on the launch stream; `cpu_baseline` is
+with HIP events the library records around it on the launch stream (timestamp-only
+events: created with hipEventDisableSystemFence, so recording one flushes no cache);
+`cpu_baseline` is
 the CPU oracle timed on a bounded sample of the same prefill workload.
 Rank 0 prints one JSON line on stdout; progress goes to stderr.
 """
@@ -120,6 +122,53 @@ def make_events(n):
     return evs
 
 
+class TimingEvent:
+    """A HIP event that only takes a timestamp (hipEventDisableSystemFence): recording it
+    neither writes back nor invalidates caches.  A default event does both when it is
+    recorded, which, placed between two kernels, slows the kernel that follows (the T=1024
+    flash kernel by ~10 % in kernel traces).  Used for the events the library records right
+    before and after a kernel; read after a device synchronize."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def hip(cls):
+        import ctypes
+        if cls._hip is None:
+            with open("/proc/self/maps") as f:   # the HIP runtime torch has loaded
+                path = next(line.split()[-1] for line in f if "libamdhip64" in line)
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        ev = ctypes.c_void_p()
+        if self.hip().hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.cuda_event = ev.value
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        if self.hip().hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                          ctypes.c_void_p(end.cuda_event)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        import ctypes
+        if self._hip is not None and getattr(self, "cuda_event", None):
+            self._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+
+
+def timing_events(n):
+    return [TimingEvent() for _ in range(n)]
+
+
 def bench_prefill(kv, W, name, steps, warmup):
     import torch
     cfg = W.CONFIGS[name]
@@ -142,8 +191,8 @@ def bench_prefill(kv, W, name, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    # per-launch duration of the flash kernel (events recorded by the library)
-    evb, eva = make_events(steps), make_events(steps)
+    # per-launch duration of the flash kernel (timestamp-only events recorded by the library)
+    evb, eva = timing_events(steps), timing_events(steps)
     for i in range(steps):
         kv.set_profile_events(evb[i], eva[i])
         call()
@@ -188,8 +237,9 @@ def bench_decode(kv, W, name, steps, warmup):
         cb[i].record()
     torch.cuda.synchronize()
     call_ms = sum(ca[i].elapsed_time(cb[i]) for i in range(steps)) / steps
-    # the attention kernel alone, in a pass of its own: the library's events around it
-    evb, eva = make_events(steps), make_events(steps)
+    # the attention kernel alone, in a pass of its own: the library's (timestamp-only)
+    # events around it
+    evb, eva = timing_events(steps), timing_events(steps)
     for i in range(steps):
         flush.sum()
         kv.set_profile_events(evb[i], eva[i])
