@@ -110,14 +110,15 @@ __device__ inline const char *uniform_ptr(const char *ptr)
 // region at `dst`: 8 instructions of 4 rows (1 KB) each; lane L takes row 4 i + L / 16 and
 // the global chunk that lands in LDS chunk L % 16 of that row (off: the per-lane byte
 // offsets, rows clamped to the last valid one).  Not tracked by the compiler: waited for
-// with an explicit vmcnt.
+// with an explicit vmcnt.  The s_nop: the wait state an LDS DMA needs after the scalar
+// write of M0 that gives its destination.
 __device__ inline void dma_tile(const char *rows, const uint32_t (&off)[8], uint32_t dst)
 {
     const char *t = uniform_ptr(rows);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t d = __builtin_amdgcn_readfirstlane(dst + (uint32_t)(4 * i * ROWB));
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
                      : "s"(d), "v"(off[i]), "s"(t)
                      : "memory", "m0");

@@ -59,6 +59,7 @@ __device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t
 // DMA of one 128-row x 64-column tile (rows past `rows` clamp to the last row) into LDS at
 // `dst`: 16 instructions of 1 KB, four per wave; lane L of instruction g fills LDS row
 // 8 g + L / 8, physical chunk L % 8, which holds logical chunk (L % 8) ^ ((row >> 1) & 7).
+// (s_nop: the wait state an LDS DMA needs after the scalar write of M0, its destination)
 __device__ inline void dma_tile(const uint16_t *base, int ld, int rows, int k0, uint32_t dst, int wave, int lane)
 {
 #pragma unroll
@@ -69,7 +70,7 @@ __device__ inline void dma_tile(const uint16_t *base, int ld, int rows, int k0, 
         const int src_row = min(row, rows - 1);
         const uint32_t off = (uint32_t)(((int64_t)src_row * ld + k0 + 8 * c) * 2);
         const uint32_t d = __builtin_amdgcn_readfirstlane(dst + (uint32_t)(g * 1024));
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
                      : "s"(d), "v"(off), "s"(base)
                      : "memory", "m0");

@@ -205,6 +205,8 @@ __device__ inline const char *uniform_ptr(const char *ptr)
 // K rows of one tile straight into an LDS stage.  `tile` is the wave-uniform address of
 // the tile's first row; the loads are inline asm so the compiler does not track them;
 // they are waited for explicitly (vmcnt) before the barrier that publishes the stage.
+// An LDS DMA reads its destination from M0 one wait state after the scalar write of M0
+// at the earliest (the s_nop; the compiler puts the same wait after its own M0 writes).
 template <bool PP>
 __device__ inline void dma_k(const char *tile, const uint32_t (&off)[Lay<PP>::NDMA], uint32_t stage_lds, int wave)
 {
@@ -213,7 +215,7 @@ __device__ inline void dma_k(const char *tile, const uint32_t (&off)[Lay<PP>::ND
     for (int i = 0; i < Lay<PP>::NDMA; ++i) {
         const uint32_t dst =
             __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)((Lay<PP>::ROWS * wave + 4 * i) * ROWB));
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
                      : "s"(dst), "v"(off[i]), "s"(t)
                      : "memory", "m0");
