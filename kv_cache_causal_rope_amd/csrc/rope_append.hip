@@ -104,8 +104,16 @@ __global__ void __launch_bounds__(256) append_kernel(uint16_t *__restrict__ cach
 
 // Fused prefill step 1: rotate new k (fp64 -> f16 RNE) and write k, v to cache rows
 // [lens[u], lens[u] + t).  One thread per (unit, token, 16-byte chunk), looping over
-// the KV heads so the trig of a (token, pair) is computed once.
-__global__ void __launch_bounds__(256) rope_append_kernel(
+// the KV heads so the trig of a (token, pair) is computed once.  The loads a thread needs
+// before its first store go out together, ahead of any use: the unit's counts, the
+// token's position, the rotation inputs and head 0's k and v chunks (from addresses that
+// do not depend on the loaded counts); a unit or row that is not appended discards them.
+// One instance per pairing, each with its own register allocation: the adjacent pairing's
+// uses 66 VGPRs (7 waves a SIMD) instead of the 108 (4) that the half-split path's eight
+// factors a thread cost a shared one (T = 1024 28-layer prefill: 17.8 -> 14.5 us).
+template <bool HALF>
+__global__ void __launch_bounds__(256)
+rope_append_kernel(
     uint16_t *__restrict__ cache_k, uint16_t *__restrict__ cache_v,
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ positions, const int32_t *__restrict__ lens,
@@ -120,53 +128,63 @@ __global__ void __launch_bounds__(256) rope_append_kernel(
     const int i = (int)(ti % t);
     const int u = (int)(ti / t);
     const int len = lens ? lens[u] : 0;
-    if (len < 0 || len > max_len)
+    const int tu = new_lens ? new_lens[u] : t;
+    const int pos = positions[ti];
+    const int set = rope_set(tab, u);
+    const int64_t src = ((int64_t)u * t + i) * hkv * kHeadDim; // head 0's row of token i
+    auto dst_row = [&](int g) { return (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim; };
+    if (!HALF) {
+        int j[4];
+        chunk_pairs(c, tab, j);
+        TrigIn<4> tin;
+        trig_load(j, pos, tab, set, tin);
+        // the k and v chunks of head 0 (the other heads' after it is stored)
+        const uint4 *ks = reinterpret_cast<const uint4 *>(k + src) + c;
+        const uint4 *vs = reinterpret_cast<const uint4 *>(v + src) + c;
+        const uint4 k0 = ks[0], v0 = vs[0];
+        double cs[4], sn[4];
+        chunk_trig_eval(c, pos, tab, set, tin, cs, sn);
+        const bool rotated = 8 * c + 7 >= tab.off;
+        auto put = [&](int g, uint4 kc, uint4 vc) {
+            Chunk16 in, out;
+            in.v = kc;
+            if (rotated)
+                rotate_chunk_f64(in.h, out.h, c, cs, sn, tab.off);
+            else
+                out.v = in.v;
+            const int64_t d = dst_row(g);
+            reinterpret_cast<uint4 *>(cache_k + d)[c] = out.v;
+            reinterpret_cast<uint4 *>(cache_v + d)[c] = vc;
+        };
+        // a padding row or an invalid count appends nothing; tested only here, after the
+        // loads, so that the compiler keeps them ahead of the wait for the counts
+        if (len < 0 || len > max_len || (new_lens && (tu < 0 || tu > t || i >= tu)))
+            return;
+        put(0, k0, v0);
+        for (int g = 1; g < hkv; ++g)
+            put(g, ks[g * (kHeadDim / 8)], vs[g * (kHeadDim / 8)]);
         return;
-    if (new_lens) {
-        const int tu = new_lens[u];
-        if (tu < 0 || tu > t || i >= tu)
-            return; // padding row, or an invalid count: nothing appended
     }
-    if (tab.half) {
-        // chunks before `off` copy K; a first-half chunk rotates with its partner and
-        // writes both; a second-half chunk only copies V
-        const int first_chunk = tab.off >> 3, h8 = tab.n_pairs >> 3;
-        const int pos = positions[ti];
-        const int set = rope_set(tab, u);
-        for (int g = 0; g < hkv; ++g) {
-            const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
-            const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
-            const uint4 *ks = reinterpret_cast<const uint4 *>(k + src);
-            uint4 *kd = reinterpret_cast<uint4 *>(cache_k + dst);
-            if (c < first_chunk) {
-                kd[c] = ks[c];
-            } else if (c < first_chunk + h8) {
-                Chunk16 a, b, ya, yb;
-                a.v = ks[c];
-                b.v = ks[c + h8];
-                rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab, set);
-                kd[c] = ya.v;
-                kd[c + h8] = yb.v;
-            }
-            reinterpret_cast<uint4 *>(cache_v + dst)[c] = reinterpret_cast<const uint4 *>(v + src)[c];
-        }
-        return;
-    }
-    double cs[4], sn[4];
-    const bool rotated = 8 * c + 7 >= tab.off;
-    if (rotated)
-        chunk_trig(c, positions[ti], tab, rope_set(tab, u), cs, sn);
+    // chunks before `off` copy K; a first-half chunk rotates with its partner and
+    // writes both; a second-half chunk only copies V
+    if (len < 0 || len > max_len || (new_lens && (tu < 0 || tu > t || i >= tu)))
+        return; // padding row, or an invalid count: nothing appended
+    const int first_chunk = tab.off >> 3, h8 = tab.n_pairs >> 3;
     for (int g = 0; g < hkv; ++g) {
-        const int64_t src = (((int64_t)u * t + i) * hkv + g) * kHeadDim;
-        const int64_t dst = (((int64_t)u * hkv + g) * s_cap + len + i) * kHeadDim;
-        Chunk16 in, out;
-        in.v = reinterpret_cast<const uint4 *>(k + src)[c];
-        if (rotated)
-            rotate_chunk_f64(in.h, out.h, c, cs, sn, tab.off);
-        else
-            out.v = in.v;
-        reinterpret_cast<uint4 *>(cache_k + dst)[c] = out.v;
-        reinterpret_cast<uint4 *>(cache_v + dst)[c] = reinterpret_cast<const uint4 *>(v + src)[c];
+        const uint4 *ks = reinterpret_cast<const uint4 *>(k + src + g * kHeadDim);
+        uint4 *kd = reinterpret_cast<uint4 *>(cache_k + dst_row(g));
+        if (c < first_chunk) {
+            kd[c] = ks[c];
+        } else if (c < first_chunk + h8) {
+            Chunk16 a, b, ya, yb;
+            a.v = ks[c];
+            b.v = ks[c + h8];
+            rotate_half_chunks(a.h, b.h, ya.h, yb.h, 8 * (c - first_chunk), pos, tab, set);
+            kd[c] = ya.v;
+            kd[c + h8] = yb.v;
+        }
+        reinterpret_cast<uint4 *>(cache_v + dst_row(g))[c] =
+            reinterpret_cast<const uint4 *>(v + src + g * kHeadDim)[c];
     }
 }
 
@@ -205,8 +223,9 @@ hipError_t launch_rope_append(uint16_t *cache_k, uint16_t *cache_v, const uint16
     const int64_t threads = (int64_t)n * t * 16;
     if (threads == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(rope_append_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
-                       cache_k, cache_v, k, v, positions, lens, new_lens, max_len, n, t, hkv, s_cap, tab);
+    hipLaunchKernelGGL(tab.half ? rope_append_kernel<true> : rope_append_kernel<false>, dim3(grid_for(threads, 256)),
+                       dim3(256), 0, stream, cache_k, cache_v, k, v, positions, lens, new_lens, max_len, n, t,
+                       hkv, s_cap, tab);
     return hipGetLastError();
 }
 

@@ -81,18 +81,85 @@ __device__ inline void pair_factor(int j, int pos, const RopeTable &tab, int set
     }
 }
 
-// adjacent pairing: the factors of the four pairs of chunk c (identity before `off`)
-__device__ inline void chunk_trig(int c, int pos, const RopeTable &tab, int set, double (&cs)[4],
-                                  double (&sn)[4])
+// The table entries the factors of N pairs are computed from, read before any of them is
+// used: from clamped indices (a pair before `off`, an invalid set or a position the table
+// does not cover reads a valid entry that is then discarded), so that the loads of all N
+// go out together instead of one round trip after another.
+template <int N> struct TrigIn {
+    double w[N];   // revolutions per position (computed angles)
+    double ms;     // output scale of the set
+    float tc[N];   // caller table entries (tables)
+    float ts[N];
+};
+template <int N>
+__device__ inline void trig_load(const int (&j)[N], int pos, const RopeTable &tab, int set, TrigIn<N> &in)
+{
+    const int sc = set < 0 ? 0 : set;
+    if (tab.cos_t) {
+        const int64_t rb = (int64_t)((pos >= 0 && pos < tab.rows) ? pos : 0) * tab.n_pairs;
+#pragma unroll
+        for (int m = 0; m < N; ++m) {
+            const int jj = min(max(j[m], 0), tab.n_pairs - 1);
+            in.tc[m] = tab.cos_t[rb + jj];
+            in.ts[m] = tab.sin_t[rb + jj];
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < N; ++m)
+            in.w[m] = tab.wrev[sc][min(max(j[m], 0), kMaxPairs - 1)];
+        in.ms = tab.mscale[sc];
+    }
+}
+// c and s of pair m from its loaded entries, as pair_factor computes them
+template <int N>
+__device__ inline void trig_eval(int m, int pos, const RopeTable &tab, int set, const TrigIn<N> &in, double &c,
+                                 double &s)
+{
+#pragma clang fp contract(off)
+    if (set < 0) {
+        c = s = __builtin_nan("");
+    } else if (tab.cos_t) {
+        if (pos >= 0 && pos < tab.rows) {
+            c = (double)in.tc[m];
+            s = (double)in.ts[m] * tab.sgn;
+        } else {
+            c = s = __builtin_nan("");
+        }
+    } else {
+        double sv, cv;
+        sincos_turns((double)pos * in.w[m], sv, cv);
+        c = cv * in.ms;
+        s = sv * in.ms * tab.sgn;
+    }
+}
+
+// adjacent pairing: the rotated pairs of chunk c (dims 8c .. 8c+7)
+__device__ inline void chunk_pairs(int c, const RopeTable &tab, int (&j)[4])
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        j[m] = (8 * c + 2 * m - tab.off) >> 1; // negative: a pair before `off`
+}
+// the factors of the four pairs of chunk c (identity before `off`) from loaded entries
+__device__ inline void chunk_trig_eval(int c, int pos, const RopeTable &tab, int set, const TrigIn<4> &in,
+                                       double (&cs)[4], double (&sn)[4])
 {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int dim = 8 * c + 2 * m;
         cs[m] = 1.0;
         sn[m] = 0.0;
-        if (dim >= tab.off)
-            pair_factor((dim - tab.off) >> 1, pos, tab, set, cs[m], sn[m]);
+        if (8 * c + 2 * m >= tab.off)
+            trig_eval(m, pos, tab, set, in, cs[m], sn[m]);
     }
+}
+__device__ inline void chunk_trig(int c, int pos, const RopeTable &tab, int set, double (&cs)[4],
+                                  double (&sn)[4])
+{
+    int j[4];
+    chunk_pairs(c, tab, j);
+    TrigIn<4> in;
+    trig_load(j, pos, tab, set, in);
+    chunk_trig_eval(c, pos, tab, set, in, cs, sn);
 }
 
 // half-split pairing: chunk c0 of the first rotated half and its partner chunk
@@ -101,10 +168,16 @@ __device__ inline void rotate_half_chunks(const uint16_t (&a)[8], const uint16_t
                                           uint16_t (&yb)[8], int j0, int pos, const RopeTable &tab, int set)
 {
 #pragma clang fp contract(off)
+    int j[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        j[e] = j0 + e;
+    TrigIn<8> in;
+    trig_load(j, pos, tab, set, in);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         double c, s;
-        pair_factor(j0 + e, pos, tab, set, c, s);
+        trig_eval(e, pos, tab, set, in, c, s);
         const double x0 = h2d(a[e]);
         const double x1 = h2d(b[e]);
         ya[e] = f64_to_f16_rne_dev(x0 * c - x1 * s);
