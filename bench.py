@@ -49,35 +49,35 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 # figure no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC = {
     "prefill_attn:qwen1p5b_prefill_t1024": {
-        "bytes": 2.7360e+08,
-        "src": ("1b6e24a75670c06300e54ab5d380f1b3983d3dd0900ed82fbd520039780504a4",
+        "bytes": 2.7341e+08,
+        "src": ("5e7ebc778f48f6ce2728ebcb49602a016a0580024a7e0c10b8b7ddf2ce7276ba",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
-                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+                "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "prefill_attn:h4096_prefill_kv_3840p256": {
         "bytes": 2.6894e+08,
-        "src": ("1b6e24a75670c06300e54ab5d380f1b3983d3dd0900ed82fbd520039780504a4",
+        "src": ("5e7ebc778f48f6ce2728ebcb49602a016a0580024a7e0c10b8b7ddf2ce7276ba",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
-                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+                "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:qwen1p5b_decode_l4096_b32": {
-        "bytes": 2.8410e+09,
-        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
+        "bytes": 2.8411e+09,
+        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
-                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+                "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:yarn_decode_l32k_b64": {
-        "bytes": 2.3068e+10,
-        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
+        "bytes": 2.3069e+10,
+        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
-                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+                "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:qwen1p5b_decode_l1024_b1": {
         "bytes": 3.0551e+07,
-        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
+        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
-                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+                "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:qwen1p5b_decode_l4096_b1": {
-        "bytes": 7.2229e+07,
-        "src": ("5375b4efc467d14456ba29e4ae6618fa83edd064ae2dab365a8d07493b4f84a0",
+        "bytes": 7.2235e+07,
+        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
-                "2f747c4fccb9ea2eff3663699a91f231af156d7ee1664df1888e2b6f4da22853")},
+                "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
 }
 KERNEL_SOURCES = {"prefill_attn": "prefill.hip", "decode_attn": "decode.hip"}
 

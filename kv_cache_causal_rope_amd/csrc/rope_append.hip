@@ -36,13 +36,14 @@ inline int rope_chunks(const RopeTable &tab)
 
 // x[rows, h, 128] rotated in place, rows = units x t; one thread per (row, 16-byte chunk
 // of the rotated region), looping over the heads so the trig is shared by all heads of a
-// row.
+// row.  One instance per pairing (own register allocation, as for rope_append_kernel).
+template <bool HALF>
 __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict__ x,
                                                            const int32_t *__restrict__ positions,
                                                            int64_t rows, int t, int h, RopeTable tab)
 {
     const int first_chunk = tab.off >> 3;
-    const int nchunks = tab.half ? tab.n_pairs >> 3 : (kHeadDim >> 3) - first_chunk;
+    const int nchunks = HALF ? tab.n_pairs >> 3 : (kHeadDim >> 3) - first_chunk;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= rows * nchunks)
         return;
@@ -50,7 +51,7 @@ __global__ void __launch_bounds__(256) rope_inplace_kernel(uint16_t *__restrict_
     const int64_t r = idx / nchunks;
     const int pos = positions[r];
     const int set = rope_set(tab, (int)(r / t));
-    if (tab.half) {
+    if (HALF) {
         const int c2 = c + (tab.n_pairs >> 3);
         for (int hh = 0; hh < h; ++hh) {
             uint4 *p = reinterpret_cast<uint4 *>(x + (r * h + hh) * kHeadDim);
@@ -198,8 +199,8 @@ hipError_t launch_rope_inplace(uint16_t *x, const int32_t *positions, int64_t ro
     const int64_t threads = rows * rope_chunks(tab);
     if (threads == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(rope_inplace_kernel, dim3(grid_for(threads, 256)), dim3(256), 0, stream,
-                       x, positions, rows, t, h, tab);
+    hipLaunchKernelGGL(tab.half ? rope_inplace_kernel<true> : rope_inplace_kernel<false>,
+                       dim3(grid_for(threads, 256)), dim3(256), 0, stream, x, positions, rows, t, h, tab);
     return hipGetLastError();
 }
 
