@@ -276,7 +276,7 @@ def check_decode(d, out, ref, lens, what):
     (3, 4, 4, [257, 2, 90], W.PLAIN_128),                # G = 1
     (2, 32, 2, [1500, 333], W.PLAIN_128),                # G = 16: two head slices
     (2, 6, 2, [4500, 2049], W.PLAIN_128),                # G = 3, multi-chunk
-    (3, 16, 8, [127, 128, 129], W.PLAIN_128),            # G = 2, chunk boundaries
+    (3, 16, 8, [255, 256, 257], W.PLAIN_128),            # G = 2, chunk boundaries (256-key minimum)
     (3, 10, 2, [40, 1700, 3], W.PLAIN_128),              # G = 5
     (2, 14, 2, [900, 77], W.YARN_TAIL_64),               # G = 7
 ])
