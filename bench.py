@@ -60,22 +60,22 @@ TRAFFIC = {
                 "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:qwen1p5b_decode_l4096_b32": {
         "bytes": 2.8411e+09,
-        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
+        "src": ("6a983c6e07b32f232012d0e5df5d4bccc196a7216bb1dc9218f3accee79e27e4",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:yarn_decode_l32k_b64": {
         "bytes": 2.3069e+10,
-        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
+        "src": ("6a983c6e07b32f232012d0e5df5d4bccc196a7216bb1dc9218f3accee79e27e4",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:qwen1p5b_decode_l1024_b1": {
-        "bytes": 3.0551e+07,
-        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
+        "bytes": 2.9481e+07,
+        "src": ("6a983c6e07b32f232012d0e5df5d4bccc196a7216bb1dc9218f3accee79e27e4",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
     "decode_attn:qwen1p5b_decode_l4096_b1": {
         "bytes": 7.2235e+07,
-        "src": ("bb9926a222f1a6db723c75473e8772c250c8602976fd6ce57a9468078059b35c",
+        "src": ("6a983c6e07b32f232012d0e5df5d4bccc196a7216bb1dc9218f3accee79e27e4",
                 "a6d9dc8cd7255542c7eebeaa1756c1c71e09d777b53c8423adfc8fdfbedf5469",
                 "3ebd6c561bb7e991ea26ae7ef7503854843410a2f2f1c272b5aca5cf584d513d")},
 }
