@@ -158,6 +158,22 @@ def test_decode_validation_and_workspace(kv):
     assert L.attn_workspace_size(kv.ATTN_OP_DECODE, n, 1, 13, 2, 128, 10) == 0
 
 
+def test_decode_split_sizes(kv):
+    """The decode split (host arithmetic only): chunks of 256 to 1024 keys, a multiple of
+    32, about two workgroups' worth per compute unit; the workspace holds one partial per
+    (unit, head, chunk) of the longest cache."""
+    for n, hq, hkv, max_len, expect in [(28, 12, 2, 1024, 256),      # one sequence, rows to 1024
+                                        (28, 12, 2, 4095, 448),      # rows to 4096
+                                        (896, 12, 2, 4096, 1024),    # 28 layers x batch 32
+                                        (256, 64, 8, 32768, 1024),   # YaRN 32k batch 64
+                                        (1, 8, 8, 10, 256)]:
+        chunk = kv.decode_chunk_keys(n, hq, hkv, max_len)
+        assert chunk == expect, (n, hq, hkv, max_len, chunk)
+        assert 256 <= chunk <= 1024 and chunk % 32 == 0
+        nsplit = (max_len + 1 + chunk - 1) // chunk
+        assert kv.workspace_size(n, hq, hkv, max_len) == n * hq * nsplit * 130 * 4
+
+
 def test_append_and_rope_validation(kv):
     L = kv.lib()
     rp = kv.RopeParams.plain()
