@@ -361,10 +361,11 @@ def bench_projections(kv, steps, warmup):
     return res
 
 
-def oracle_time(W, name, units, threads):
+def oracle_time(W, name, units, threads, min_sec=0.0, max_runs=1):
     """Seconds the oracle (untuned, fp64, OpenMP on `threads` threads) takes for `units`
-    layers of a prefill workload, run in this process (which touches no GPU); prints one
-    JSON line."""
+    layers of a prefill workload, run in this process (which touches no GPU): the mean of
+    repeated runs until `min_sec` of work or `max_runs` runs (each run appends the same rows
+    again, so every run does the same work); prints one JSON line."""
     import numpy as np
     import torch
     import oracle
@@ -377,12 +378,16 @@ def oracle_time(W, name, units, threads):
                            ext_factor=r.ext_factor, n_ctx_orig=r.n_ctx_orig, beta_fast=r.beta_fast,
                            beta_slow=r.beta_slow, mscale=r.mscale)
     oracle.set_num_threads(threads)
-    t0 = time.perf_counter()
-    oracle.prefill_kv(bits(inp.q), bits(inp.k), bits(inp.v), inp.positions.numpy(), ck, cv,
-                      inp.lens.numpy(), cfg.scale, rp)
-    sec = time.perf_counter() - t0
+    args = (bits(inp.q), bits(inp.k), bits(inp.v), inp.positions.numpy(), ck, cv, inp.lens.numpy(), cfg.scale, rp)
+    total, runs = 0.0, 0
+    while runs < max(1, max_runs) and (runs == 0 or total < min_sec):
+        t0 = time.perf_counter()
+        oracle.prefill_kv(*args)
+        total += time.perf_counter() - t0
+        runs += 1
     flops = prefill_flops(units, cfg.t, cfg.hq, cfg.d, inp.lens.numpy())
-    print(json.dumps({"sec": sec, "flops": flops, "threads": oracle.num_threads()}), flush=True)
+    print(json.dumps({"sec": total / runs, "runs": runs, "total_sec": total, "flops": flops,
+                      "threads": oracle.num_threads()}), flush=True)
 
 
 def cpu_baseline(name, st_units):
@@ -392,9 +397,10 @@ def cpu_baseline(name, st_units):
     import subprocess
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
 
-    def run(workload, units, nthreads):
+    def run(workload, units, nthreads, min_sec=0.0, max_runs=1):
         out = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-time", workload, str(units),
-                              str(nthreads)], capture_output=True, text=True, check=True).stdout
+                              str(nthreads), str(min_sec), str(max_runs)],
+                             capture_output=True, text=True, check=True).stdout
         return json.loads(out.strip().splitlines()[-1])
 
     model = "unknown"
@@ -405,13 +411,14 @@ def cpu_baseline(name, st_units):
                 break
     except OSError:
         pass
-    full = run(name, 28, threads)
+    full = run(name, 28, threads, min_sec=10.0, max_runs=30)  # about 10 s of work
     tiny = run("tiny_prefill_t64", 1, 1)
     one = run(name, st_units, 1)
     return {"value": full["flops"] / full["sec"] / 1e12, "unit": "TFLOP/s", "cores": full["threads"],
             "kind": "oracle",
             "sample": f"all 28 layers of {name} (T=1024, 12q/2kv x 128), full causal prefill incl. "
-                      f"rotary + append, {full['sec']:.1f} s on {full['threads']} threads",
+                      f"rotary + append, {full['sec']:.2f} s per run on {full['threads']} threads, "
+                      f"mean of {full['runs']} runs ({full['total_sec']:.1f} s)",
             "cpu_model": model,
             "single_thread": {
                 "threads": one["threads"],
@@ -429,7 +436,7 @@ def main():
     ap.add_argument("--workload", default="qwen1p5b_prefill_t1024")
     ap.add_argument("--cpu-single-thread-units", type=int, default=4,
                     help="layers of the prefill workload the single-thread oracle run takes")
-    ap.add_argument("--oracle-time", nargs=3, metavar=("WORKLOAD", "UNITS", "THREADS"),
+    ap.add_argument("--oracle-time", nargs=5, metavar=("WORKLOAD", "UNITS", "THREADS", "MIN_SEC", "MAX_RUNS"),
                     help=argparse.SUPPRESS)  # child process of the CPU baseline
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -442,7 +449,8 @@ def main():
     args = ap.parse_args()
     if args.oracle_time:
         from kv_cache_causal_rope_amd import workloads as W
-        oracle_time(W, args.oracle_time[0], int(args.oracle_time[1]), int(args.oracle_time[2]))
+        oracle_time(W, args.oracle_time[0], int(args.oracle_time[1]), int(args.oracle_time[2]),
+                    float(args.oracle_time[3]), int(args.oracle_time[4]))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this attention path runs on a single MI355X "
