@@ -133,6 +133,8 @@ def test_prefill_tiny_workload(kv):
     (1, 40, 32, 2),   # G = 16: two head slices per workgroup group
     (2, 1, 12, 2),    # single token
     (1, 130, 8, 4),   # G = 2
+    (2, 70, 8, 1),    # one KV head (G = 8): the append kernel's single-head path
+    (1, 48, 8, 8),    # eight KV heads, G = 1
 ])
 def test_prefill_shapes(kv, n, t, hq, hkv):
     cfg = custom(n, t, hq, hkv, t + 3, seed=200 + t)
@@ -279,6 +281,7 @@ def check_decode(d, out, ref, lens, what):
     (3, 16, 8, [255, 256, 257], W.PLAIN_128),            # G = 2, chunk boundaries (256-key minimum)
     (3, 10, 2, [40, 1700, 3], W.PLAIN_128),              # G = 5
     (2, 14, 2, [900, 77], W.YARN_TAIL_64),               # G = 7
+    (3, 8, 1, [600, 5, 1300], W.PLAIN_128),              # one KV head, G = 8
 ])
 def test_decode_shapes(kv, n, hq, hkv, lens, rope):
     d, out, ref = run_decode(kv, n, hq, hkv, lens, max(lens) + 3, rope, seed=500 + n)
