@@ -96,24 +96,22 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmParams p, RopeTable tab)
     const int lane = tid & 63;
     const int tiles_m = (p.rows_u + TM - 1) / TM;
     const int tiles_n = p.n / TN;
+    // Tile order: layer, then row tile, then column tile (for QKV the k heads' columns
+    // first: their rotating epilogue takes about twice as long).  Workgroups are dealt to
+    // the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; when the grid is a multiple
+    // of 8, XCD x takes the contiguous range of tiles [x B/8, (x+1) B/8) in order, and the
+    // ~64 workgroups it runs at a time share a few A row panels and W column panels in its
+    // L2 instead of every XCD fetching every layer's operands.
     int b = blockIdx.x, tn;
-    if (EPI == EPI_QKV) {
-        // the k-head tiles (rotation in the epilogue, about twice as long) go first, so
-        // that they are not left for the last round
-        const int nk = p.units * tiles_m * p.hkv;
-        if (b < nk) {
-            tn = p.hq + b % p.hkv;
-            b /= p.hkv;
-        } else {
-            b -= nk;
-            const int others = tiles_n - p.hkv, t = b % others;
-            tn = t < p.hq ? t : t + p.hkv;
-            b /= others;
-        }
-    } else {
-        tn = b % tiles_n;
-        b /= tiles_n;
-    }
+    const int nblk = (int)gridDim.x;
+    if ((nblk & 7) == 0)
+        b = (b & 7) * (nblk >> 3) + (b >> 3);
+    const int j = b % tiles_n;
+    b /= tiles_n;
+    if (EPI == EPI_QKV)
+        tn = j < p.hkv ? p.hq + j : (j < p.hkv + p.hq ? j - p.hkv : j);
+    else
+        tn = j;
     const int tm = b % tiles_m;
     const int u = b / tiles_m;
     const int m0 = tm * TM, n0 = tn * TN;
