@@ -96,8 +96,9 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmParams p, RopeTable tab)
     const int lane = tid & 63;
     const int tiles_m = (p.rows_u + TM - 1) / TM;
     const int tiles_n = p.n / TN;
-    // Tile order: layer, then row tile, then column tile (for QKV the k heads' columns
-    // first: their rotating epilogue takes about twice as long).  Workgroups are dealt to
+    // Tile order: layer, then row tile, then column tile (QKV: layer, column tile with the
+    // k heads' columns first, whose rotating epilogue takes about twice as long, then row
+    // tile).  Workgroups are dealt to
     // the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; when the grid is a multiple
     // of 8, XCD x takes the contiguous range of tiles [x B/8, (x+1) B/8) in order, and the
     // ~64 workgroups it runs at a time share a few A row panels and W column panels in its
@@ -106,14 +107,21 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmParams p, RopeTable tab)
     const int nblk = (int)gridDim.x;
     if ((nblk & 7) == 0)
         b = (b & 7) * (nblk >> 3) + (b >> 3);
-    const int j = b % tiles_n;
-    b /= tiles_n;
-    if (EPI == EPI_QKV)
+    int tm, u;
+    if (EPI == EPI_QKV) {
+        // column tile outside the row tile: the layer's fused weight (6 MB at hidden 1536)
+        // outgrows an XCD's L2, so its resident workgroups share fewer weight panels
+        tm = b % tiles_m;
+        b /= tiles_m;
+        const int j = b % tiles_n;
+        u = b / tiles_n;
         tn = j < p.hkv ? p.hq + j : (j < p.hkv + p.hq ? j - p.hkv : j);
-    else
-        tn = j;
-    const int tm = b % tiles_m;
-    const int u = b / tiles_m;
+    } else {
+        tn = b % tiles_n;
+        b /= tiles_n;
+        tm = b % tiles_m;
+        u = b / tiles_m;
+    }
     const int m0 = tm * TM, n0 = tn * TN;
     const int rows = min(TM, p.rows_u - m0);
 
